@@ -1,0 +1,143 @@
+"""Seeded synthetic workloads: sequence structure and random bf16 Q/K/V.
+
+This module is the one place both sides of a parity check draw their inputs
+from.  It holds the *shape* of each workload (which visual grids and audio
+runs make up each packed sequence, in reference order) and a seeded random
+number recipe.  It holds none of the method's arithmetic: it does not compute
+positions, rotations or attention.  The layout rules named here ("attached",
+"rule") are interpreted independently by the library's layout builder and by
+the oracle.
+
+Item vocabulary (one dict per item, items listed in reference order):
+
+* ``{"kind": "visual", "T": T, "H": H, "W": W}`` -- a latent video grid
+  (an image reference is a grid with T = 1).
+* ``{"kind": "audio", "n": n, "span": s, "attached": bool, "rule": r}`` --
+  a run of ``n`` audio latent rows covering ``s`` latent frames of the shared
+  clock.  ``attached`` audio rides the clock span of the visual item just
+  before it (a video's own soundtrack); a standalone audio reference starts at
+  the current clock and advances it by ``s``.  ``rule`` is ``"linear"``
+  (offset i*s/n) or ``"round"`` (that offset rounded half-to-even).
+
+The workloads follow the sequence structure the pages describe: the DiT packs
+the video latent and the audio latent into one long token sequence
+("Day 0 Support for MiniMax-H3 on AMD Instinct GPUs", section "The diffusion
+transformer (DiT)"); references sit in front of the generated rows, in
+reference order, on one shared audio/video rotary clock ("minimax-h3-reference"
+Space README, sections "References" and "AoTI-compiled blocks"); co-batched
+requests are packed with one attention document each (vLLM-Omni "MiniMax-H3"
+recipe, section "Step execution and continuous batching").
+
+Random inputs: ``numpy.random.Generator(PCG64(seed))``, then
+``standard_normal((N, H, D), float32)`` drawn for q, k, v in that order,
+optionally multiplied by a per-tensor factor, then rounded to bfloat16 by
+round-to-nearest-even on the float32 bit pattern.  The result is returned as
+uint16 bit patterns so that neither side needs a bfloat16 dtype to agree on
+the exact input values.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+ROPE_THETA = 10000.0
+ROPE_DIMS = (32, 48, 48)  # (t, h, w) widths inside the 128-wide head
+
+
+def visual(T: int, H: int, W: int) -> dict:
+    return {"kind": "visual", "T": int(T), "H": int(H), "W": int(W)}
+
+
+def audio(n: int, span: float, attached: bool, rule: str = "linear") -> dict:
+    assert rule in ("linear", "round")
+    return {"kind": "audio", "n": int(n), "span": float(span), "attached": bool(attached), "rule": rule}
+
+
+def _packed_segments():
+    return [[visual(T, 24, 42), audio(32 * T, T, attached=True)] for T in (5, 9, 13, 17)]
+
+
+def _ref2va_segment():
+    seg = [visual(1, 24, 42) for _ in range(9)]          # 9 image references
+    seg += [visual(8, 24, 42), audio(256, 8, attached=True)]  # reference video + its soundtrack
+    seg += [audio(256, 8, attached=False)]               # standalone reference audio
+    seg += [visual(17, 24, 42), audio(544, 17, attached=True)]  # generated target
+    return [seg]
+
+
+# The five workloads.  "heads" is the head count one GPU computes.
+CONFIGS = {
+    "tiny": {
+        "heads": 4,
+        "segments": [[visual(3, 8, 8), audio(24, 3, attached=True, rule="round")]],
+        "seed": 1,
+    },
+    "480p": {
+        "heads": 24,
+        "segments": [[visual(8, 24, 40), audio(256, 8, attached=True)]],
+        "seed": 2,
+    },
+    "packed": {
+        "heads": 16,
+        "segments": _packed_segments(),
+        "seed": 3,
+    },
+    "1344x768": {
+        "heads": 5,
+        "segments": [[visual(32, 48, 84), audio(1024, 32, attached=True)]],
+        "seed": 4,
+    },
+    "ref2va": {
+        "heads": 24,
+        "segments": _ref2va_segment(),
+        "seed": 5,
+    },
+}
+
+CONFIG_ORDER = ["tiny", "480p", "packed", "1344x768", "ref2va"]
+
+# Seed offset for the second (robustness) seed of each workload.
+ROBUSTNESS_SEED_OFFSET = 1000
+
+
+def item_rows(item: dict) -> int:
+    if item["kind"] == "visual":
+        return item["T"] * item["H"] * item["W"]
+    return item["n"]
+
+
+def n_tokens(segments) -> int:
+    return sum(item_rows(it) for seg in segments for it in seg)
+
+
+def segment_lengths(segments):
+    return [sum(item_rows(it) for it in seg) for seg in segments]
+
+
+def _round_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 bfloat16 bit patterns, round to nearest even."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def random_qkv(n: int, heads: int, seed: int, head_dim: int = HEAD_DIM, scale=(1.0, 1.0, 1.0)):
+    """Seeded bf16 q, k, v as uint16 bit patterns of shape [n, heads, head_dim]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for s in scale:
+        x = rng.standard_normal((n, heads, head_dim), dtype=np.float32)
+        if s != 1.0:
+            x = x * np.float32(s)
+        out.append(_round_bf16_bits(x))
+    return tuple(out)
+
+
+def config(name: str) -> dict:
+    return CONFIGS[name]
