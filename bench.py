@@ -1,0 +1,185 @@
+"""Benchmark: joint A/V attention TFLOP/s on the ~130k-token workload, % of bf16 MFMA peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1344x768] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over the resident synthetic batch:
+the K/V prologue (key rotation + packing) and the attention kernel (query
+rotation fused into its loads, QK^T, online softmax, PV, epilogue).  Inputs,
+positions and cu_seqlens are built once and are in HBM before timing starts.
+
+value = algorithmic FLOP per step (4 * S^2 * d per segment and head) / mean step
+time.  roofline: the attention kernel alone, timed with HIP events recorded on
+the stream it is launched on, against the bf16 dense MFMA peak.
+cpu_baseline: the float64 oracle on a bounded sample of query rows of the same
+workload, on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "joint A/V attention TFLOP/s @ ~130k tokens; % of bf16 MFMA peak"
+
+
+def describe(name, cfg, n_tokens, n_segments):
+    desc = {
+        "tiny": "tiny: 3x8x8 video + 24 audio",
+        "480p": "480p-shaped: 8x24x40 video + 256 audio",
+        "packed": "packed varlen: 4 segments (5,9,13,17)x24x42 video, each + 32*T audio",
+        "1344x768": "1344x768-shaped, one GPU's head share: 32x48x84 video + 1,024 audio",
+        "ref2va": "ref2va-shaped: 9 images + ref video/audio + ref audio + 17x24x42 target",
+    }[name]
+    return {"workload": desc, "tokens": n_tokens, "segments": n_segments, "heads": cfg["heads"], "head_dim": 128,
+            "rope": "theta 10000, t/h/w = 32/48/48", "attention": "non-causal, per segment"}
+
+
+def cpu_baseline(c, flop_per_row_head, target_seconds=15.0):
+    """Time the float64 oracle on whole query rows (all heads) of the same workload."""
+    import numpy as np
+
+    import oracle
+    from joint_sequence_attention_amd import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    q64 = wl.bf16_bits_to_f32(c["qb"]).astype(np.float64)
+    k64 = wl.bf16_bits_to_f32(c["kb"]).astype(np.float64)
+    v64 = wl.bf16_bits_to_f32(c["vb"]).astype(np.float64)
+    rng = np.random.default_rng(0)
+    rows_done, t_used, batch = 0, 0.0, 8
+    while t_used < target_seconds and rows_done < c["N"]:
+        rows = np.sort(rng.choice(c["N"], size=batch, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention_rows(q64, k64, v64, c["cu"], c["pos"], rows)
+        t_used += time.perf_counter() - t0
+        rows_done += batch
+        batch = min(batch * 2, 256)
+    flop = rows_done * c["heads"] * flop_per_row_head
+    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} random query rows x {c['heads']} heads, each against all keys of its segment "
+                      f"({t_used:.1f} s of float64 oracle time; FLOP counted as 4*S*d per row and head)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="1344x768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path runs on one GPU's head share and this build has no "
+              "multi-GPU mode (see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from joint_sequence_attention_amd import h3attn as H
+    from joint_sequence_attention_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    name = args.workload
+    cfg = wl.config(name)
+    cu, pos = H.h3attn_build_layout(cfg["segments"])
+    N, heads = int(cu[-1]), cfg["heads"]
+    lens = np.diff(cu.astype(np.int64))
+    max_seqlen = int(lens.max())
+    qb, kb, vb = wl.random_qkv(N, heads, cfg["seed"])
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    cu_d = torch.from_numpy(cu).to(dev)
+    pos_d = torch.from_numpy(np.ascontiguousarray(pos)).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((heads, N), dtype=torch.float32, device=dev)
+    ws = H.alloc_workspace(N, heads, len(lens), dev)
+    flop = H.attention_flops(cu, heads)
+
+    def step(ev_a=None, ev_b=None):
+        H.h3attn_varlen_kv_prologue(k, v, cu_d, pos_d, max_seqlen, ws)
+        if ev_a is not None:
+            ev_a.record()
+        H.h3attn_varlen_attention(q, cu_d, pos_d, max_seqlen, ws, out=out, lse=lse)
+        if ev_b is not None:
+            ev_b.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {name}: N={N} heads={heads} segments={len(lens)} FLOP/step={flop:.4e}; warmup done",
+          file=sys.stderr, flush=True)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(*evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    if not (torch.isfinite(out.float()).all() and torch.isfinite(lse).all()):
+        print("[bench] non-finite output", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] {ms_per_step:.3f} ms/step, attention kernel {attn_ms:.3f} ms -> {achieved:.1f} TFLOP/s "
+          f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of peak)", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        c = {"qb": qb, "kb": kb, "vb": vb, "cu": cu, "pos": pos, "N": N, "heads": heads}
+        # every sampled row attends to all keys of its (here single) segment
+        cpu = cpu_baseline(c, 4.0 * 128 * max_seqlen, args.cpu_seconds) if len(lens) == 1 else None
+        if cpu:
+            print(f"[bench] cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads", file=sys.stderr,
+                  flush=True)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) q/k/v; positions from the workload's grids)",
+        "config": describe(name, cfg, N, len(lens)),
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

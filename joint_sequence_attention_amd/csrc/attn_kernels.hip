@@ -1,0 +1,492 @@
+// HIP kernels for gfx950 (MI355X): multi-axis RoPE and packed varlen
+// flash-attention forward.
+//
+// The operation: every token of a packed video+audio sequence attends to
+// every token of its own segment ("Day 0 Support for MiniMax-H3 on AMD
+// Instinct GPUs", "The diffusion transformer (DiT)"; vLLM-Omni "MiniMax-H3"
+// recipe, "Step execution and continuous batching"), with queries and keys
+// turned by a rotary embedding of their (t, h, w) position.
+//
+// Three kernels:
+//   rope_apply_kernel   y = rope(x): one 16-byte chunk (8 dims) per thread.
+//   kv_prologue_kernel  rotates K once per call and packs it, with V
+//                       transposed, into 64-key tiles that start on a 64-key
+//                       boundary for every segment.  HBM-bound.
+//   attn_fwd_kernel     one workgroup per (query tile, segment, head).  It
+//                       rotates its queries while loading them, then streams
+//                       the segment's key tiles through LDS and runs an online
+//                       softmax between two bf16 MFMA contractions.
+//
+// MFMA orientation.  The score tile is computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims (from LDS), B = 16 dims x
+// 32 queries (held in registers for the whole kernel).  In the 32x32
+// accumulator, lane L owns query column L % 32 and the 16 key rows
+// 8*(r/4) + 4*(L/32) + r%4, r = 0..15; the other 16 keys of that query sit in
+// lane L ^ 32.  So a row maximum or row sum is an in-lane reduction plus one
+// v_permlane32_swap.  The probabilities then serve directly as the B operand
+// of O^T += V^T P^T (keys are the contraction index), with no data movement:
+// registers 8*hh .. 8*hh+7 of a sub-block hold 8 keys of one 16-key group.
+// The prologue stores V^T with its keys permuted inside each 16-key group so
+// that the matching A operand (8 keys of one value dim) is one contiguous
+// 16-byte LDS read.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace h3attn {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+
+constexpr int D = kHeadDim;
+constexpr int BK = kKeyTile;                    // keys per tile
+constexpr int CHUNKS_PER_ROW = D / 8;           // 16-byte chunks per 128-dim row
+constexpr int TILE_CHUNKS = BK * CHUNKS_PER_ROW;  // 1024 chunks = 16 KiB per tile
+
+__device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even), low half first.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(a);
+  v[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf_lo(v[i]);
+    f[2 * i + 1] = bf_hi(v[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+// Rotate 4 consecutive pairs (dims 2*pair0 .. 2*pair0+7) in fp32.  Pair p
+// turns by phi = pos[axis(p)] * omega(p); (x0, x1) -> (x0 cos - x1 sin,
+// x0 sin + x1 cos).  Every caller goes through this one function, so the
+// standalone RoPE and the rotation fused into the attention loads round
+// identically.
+__device__ __forceinline__ void rope8(float (&x)[8], int pair0, const float* s_omega, const int* s_axis,
+                                      float pt, float ph, float pw) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = pair0 + i;
+    const int ax = s_axis[p];
+    const float ps = ax == 0 ? pt : (ax == 1 ? ph : pw);
+    const float phi = ps * s_omega[p];
+    float sn, cs;
+    sincosf(phi, &sn, &cs);
+    const float x0 = x[2 * i], x1 = x[2 * i + 1];
+    x[2 * i] = fmaf(x0, cs, -(x1 * sn));
+    x[2 * i + 1] = fmaf(x0, sn, x1 * cs);
+  }
+}
+
+__device__ __forceinline__ void stage_rope_table(const RopeTable& tab, float* s_omega, int* s_axis) {
+  if (threadIdx.x < kPairs) {
+    s_omega[threadIdx.x] = tab.omega[threadIdx.x];
+    s_axis[threadIdx.x] = tab.axis[threadIdx.x];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone RoPE.  x and y may be the same buffer.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rope_apply_kernel(const u32x4* x, u32x4* y, const float* __restrict__ pos,
+                                                         int64_t n_chunks, int32_t chunks_per_token, RopeTable tab) {
+  __shared__ float s_omega[kPairs];
+  __shared__ int s_axis[kPairs];
+  stage_rope_table(tab, s_omega, s_axis);
+  __syncthreads();
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
+    const int64_t tok = c / chunks_per_token;
+    const int pair0 = int(c % CHUNKS_PER_ROW) * 4;
+    float f[8];
+    unpack8(x[c], f);
+    rope8(f, pair0, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
+    y[c] = pack8(f);
+  }
+}
+
+// Row of the packed workspace where segment s's first key lives.
+__device__ __forceinline__ int64_t packed_start(int32_t seg_begin, int32_t s) {
+  return int64_t(BK) * ((int64_t(seg_begin) + BK - 1) / BK + s);
+}
+
+// ---------------------------------------------------------------------------
+// K/V prologue.  grid = (key tiles of the longest segment, segments, heads).
+// k_ws: [H][rows][128] rotated keys (rows past a segment's end are zero).
+// v_ws: [H][rows/64][128][64] transposed value tiles; inside each 16-key
+//       group the 4-key runs are stored in the order 0, 2, 1, 3.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                          const int32_t* __restrict__ cu,
+                                                          const float* __restrict__ pos, int32_t n_heads,
+                                                          RopeTable tab, u32x4* __restrict__ k_ws,
+                                                          u32x2* __restrict__ v_ws, int64_t rows_per_head) {
+  __shared__ float s_omega[kPairs];
+  __shared__ int s_axis[kPairs];
+  const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int32_t seg_a = cu[s];
+  const int32_t S = cu[s + 1] - seg_a;
+  if (tile * BK >= S) return;  // whole block leaves together
+  stage_rope_table(tab, s_omega, s_axis);
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int64_t prow = packed_start(seg_a, s) + int64_t(tile) * BK;  // packed row of this tile's key 0
+
+  // Keys: 1024 chunks, 4 per thread; chunk c is row c / 16, dims 8 * (c % 16) ..
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 4, cc = c & 15;
+    const int key = tile * BK + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < S) {
+      const int64_t tok = int64_t(seg_a) + key;
+      float f[8];
+      unpack8(k[(tok * n_heads + h) * CHUNKS_PER_ROW + cc], f);
+      rope8(f, cc * 4, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
+      val = pack8(f);
+    }
+    k_ws[(int64_t(h) * rows_per_head + prow + r) * CHUNKS_PER_ROW + cc] = val;
+  }
+
+  // Values: thread owns keys 4*k4 .. 4*k4+3 and dims 8*dc .. 8*dc+7.
+  {
+    const int k4 = tid & 15, dc = tid >> 4;
+    unsigned w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = tile * BK + 4 * k4 + i;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (key < S) val = v[((int64_t(seg_a) + key) * n_heads + h) * CHUNKS_PER_ROW + dc];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[i][j] = val[j];
+    }
+    // stored position of this 4-key run inside its 16-key group
+    const int run = k4 & 3;
+    const int kpos = 16 * (k4 >> 2) + 4 * (((run & 1) << 1) | (run >> 1));
+    u32x2* vt = v_ws + (int64_t(h) * (rows_per_head / BK) + prow / BK) * (D * BK / 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // dims 8*dc + 2j (low halves) and 8*dc + 2j + 1 (high halves)
+      u32x2 lo, hi;
+      lo[0] = (w[0][j] & 0xffffu) | (w[1][j] << 16);
+      lo[1] = (w[2][j] & 0xffffu) | (w[3][j] << 16);
+      hi[0] = (w[0][j] >> 16) | (w[1][j] & 0xffff0000u);
+      hi[1] = (w[2][j] >> 16) | (w[3][j] & 0xffff0000u);
+      const int d = 8 * dc + 2 * j;
+      vt[(d * BK + kpos) / 4] = lo;
+      vt[((d + 1) * BK + kpos) / 4] = hi;
+    }
+  }
+}
+
+// Max / sum with the partner lane (L ^ 32) that holds the other 16 keys.
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Attention forward.  NW waves per workgroup, each owning QB blocks of 32
+// query rows; BQ = 32 * NW * QB query rows per workgroup.
+// grid = (query tiles of the longest segment, segments, heads).
+// ---------------------------------------------------------------------------
+constexpr int KSTR = D + 8;   // bf16 per K row in LDS (16-byte pad against bank conflicts)
+constexpr int VSTR = BK + 8;  // bf16 per V^T row in LDS
+constexpr int K_LDS_BYTES = BK * KSTR * 2;
+constexpr int V_LDS_BYTES = D * VSTR * 2;
+constexpr int STAGE_BYTES = K_LDS_BYTES + V_LDS_BYTES;
+
+template <int NW, int QB>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restrict__ q, const int32_t* __restrict__ cu,
+                                                           const float* __restrict__ pos, u32x2* __restrict__ out,
+                                                           float* __restrict__ lse, int32_t n_tokens, int32_t n_heads,
+                                                           float scale, float scale_log2, RopeTable tab,
+                                                           const u32x4* __restrict__ k_ws,
+                                                           const u32x4* __restrict__ v_ws, int64_t rows_per_head) {
+  constexpr int NT = NW * 64;
+  constexpr int BQ = NW * QB * 32;
+  constexpr int CH = TILE_CHUNKS / NT;  // chunks per thread per tensor per tile
+  static_assert(TILE_CHUNKS % NT == 0, "tile must split evenly over the workgroup");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // 2 stages
+  __shared__ float s_omega[kPairs];
+  __shared__ int s_axis[kPairs];
+
+  const int qt = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int32_t seg_a = cu[s];
+  const int32_t S = cu[s + 1] - seg_a;
+  if (qt * BQ >= S) return;  // whole block leaves together
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  stage_rope_table(tab, s_omega, s_axis);
+
+  const int n_kt = (S + BK - 1) / BK;
+  const int64_t prow = packed_start(seg_a, s);
+  const u32x4* kg = k_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
+  const u32x4* vg = v_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
+
+  // First key/value tile: issue the loads before the query rotation.
+  u32x4 kreg[CH], vreg[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    kreg[i] = kg[tid + i * NT];
+    vreg[i] = vg[tid + i * NT];
+  }
+  __syncthreads();  // rope table staged
+
+  // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 of block qb
+  // and dims 16*ks + 8*g .. +7 for ks = 0..7, rotated and rounded to bf16.
+  bf16x8 qf[QB][8];
+  int qrow[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = qt * BQ + (wave * QB + qb) * 32 + l32;
+    qrow[qb] = r;
+    if (r < S) {
+      const int64_t tok = int64_t(seg_a) + r;
+      const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
+      const u32x4* qp = q + (tok * n_heads + h) * CHUNKS_PER_ROW;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        float f[8];
+        unpack8(qp[2 * ks + g], f);
+        rope8(f, ks * 8 + g * 4, s_omega, s_axis, pt, ph, pw);
+        qf[qb][ks] = __builtin_bit_cast(bf16x8, pack8(f));
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  auto store_stage = [&](int stage) {
+    char* sk = smem + stage * STAGE_BYTES;
+    char* sv = sk + K_LDS_BYTES;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4*>(sk + ((c >> 4) * KSTR + (c & 15) * 8) * 2) = kreg[i];
+      *reinterpret_cast<u32x4*>(sv + ((c >> 3) * VSTR + (c & 7) * 8) * 2) = vreg[i];
+    }
+  };
+  store_stage(0);
+  __syncthreads();
+
+  f32x16 o[QB][4];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
+  }
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const char* sk = smem + (kt & 1) * STAGE_BYTES;
+    const char* sv = sk + K_LDS_BYTES;
+    const bool more = kt + 1 < n_kt;
+    if (more) {
+      const u32x4* kn = kg + int64_t(kt + 1) * TILE_CHUNKS;
+      const u32x4* vn = vg + int64_t(kt + 1) * TILE_CHUNKS;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        kreg[i] = kn[tid + i * NT];
+        vreg[i] = vn[tid + i * NT];
+      }
+    }
+
+    // S^T for two 32-key sub-blocks.
+    f32x16 sacc[2][QB];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][qb][r] = 0.0f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + ((32 * sb + l32) * KSTR + 16 * ks + 8 * g) * 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[sb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sacc[sb][qb], 0, 0, 0);
+      }
+    }
+
+    // Keys past the segment end (last tile only) get probability zero.
+    if (kt == n_kt - 1 && (S % BK) != 0) {
+      const int kbase = kt * BK;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= S) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[sb][qb][r] = -INFINITY;
+          }
+        }
+    }
+
+    // Online softmax (base 2, scores kept in raw units; scale folded into the exponent).
+    bf16x8 pf[QB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = sacc[0][qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][qb][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][qb][r]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m[qb], mx);
+      const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_new) * scale_log2);
+      m[qb] = m_new;
+      const float mc = m_new * scale_log2;
+      float rs = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][r], scale_log2, -mc));
+          sacc[sb][qb][r] = p;
+          rs += p;
+        }
+      l[qb] = fmaf(l[qb], alpha, rs);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(sacc[sb][qb][8 * hh + 2 * i], sacc[sb][qb][8 * hh + 2 * i + 1]);
+          pf[qb][sb][hh] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(sv + ((32 * db + l32) * VSTR + 32 * sb + 16 * hh + 8 * g) * 2);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][sb][hh], o[qb][db], 0, 0, 0);
+        }
+
+    if (more) store_stage((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = O / l, lse = scale * m + ln l.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = pair_sum(l[qb]);
+    const float inv = 1.0f / lt;
+    if (qrow[qb] < S) {
+      const int64_t tok = int64_t(seg_a) + qrow[qb];
+      u32x2* orow = out + (tok * n_heads + h) * (D / 4);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          u32x2 w;
+          w[0] = pack_bf16x2(o[qb][db][4 * k4] * inv, o[qb][db][4 * k4 + 1] * inv);
+          w[1] = pack_bf16x2(o[qb][db][4 * k4 + 2] * inv, o[qb][db][4 * k4 + 3] * inv);
+          orow[db * 8 + 2 * k4 + g] = w;
+        }
+      if (g == 0) lse[int64_t(h) * n_tokens + tok] = fmaf(m[qb], scale, logf(lt));
+    }
+  }
+}
+
+constexpr int ATTN_NW = 4;
+constexpr int ATTN_QB = 2;
+constexpr int ATTN_BQ = 32 * ATTN_NW * ATTN_QB;
+constexpr size_t ATTN_SMEM = 2 * STAGE_BYTES;
+
+}  // namespace
+
+const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,
+                      const RopeTable& table, void* stream) {
+  const int64_t n_chunks = n_tokens * n_heads * CHUNKS_PER_ROW;
+  int64_t blocks = (n_chunks + 255) / 256;
+  if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+  hipLaunchKernelGGL(rope_apply_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(x), static_cast<u32x4*>(y), pos, n_chunks,
+                     int32_t(n_heads * CHUNKS_PER_ROW), table);
+  return int(hipGetLastError());
+}
+
+int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const float* pos, int64_t /*n_tokens*/,
+                       int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws,
+                       void* v_ws, int64_t rows_per_head, void* stream) {
+  const unsigned tiles = unsigned((int64_t(max_seqlen) + BK - 1) / BK);
+  if (tiles == 0) return 0;
+  hipLaunchKernelGGL(kv_prologue_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), cu,
+                     pos, n_heads, table, static_cast<u32x4*>(k_ws), static_cast<u32x2*>(v_ws), rows_per_head);
+  return int(hipGetLastError());
+}
+
+int launch_attention(const void* q, const int32_t* cu, const float* pos, void* out, float* lse, int64_t n_tokens,
+                     int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
+                     const void* k_ws, const void* v_ws, int64_t rows_per_head, void* stream) {
+  const unsigned tiles = unsigned((int64_t(max_seqlen) + ATTN_BQ - 1) / ATTN_BQ);
+  if (tiles == 0) return 0;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<ATTN_NW, ATTN_QB>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(ATTN_SMEM));
+    if (e != hipSuccess) return int(e);
+    attr_set = true;
+  }
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((attn_fwd_kernel<ATTN_NW, ATTN_QB>), dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),
+                     dim3(ATTN_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
+                     pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale, scale_log2, table,
+                     static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), rows_per_head);
+  return int(hipGetLastError());
+}
+
+}  // namespace h3attn

@@ -1,0 +1,48 @@
+// Internal declarations shared by the host-side translation units of libh3attn.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "h3attn.h"
+
+namespace h3attn {
+
+// Thread-local error detail for h3attn_last_error().
+void clear_error();
+h3attn_status fail(h3attn_status s, const char* msg);
+
+constexpr int kHeadDim = 128;
+constexpr int kPairs = kHeadDim / 2;
+constexpr int kKeyTile = 64;  // keys per packed workspace tile
+
+// Rotary table for one call: per rotation pair p (dims 2p, 2p+1), the axis it
+// turns with (0 = t, 1 = h, 2 = w) and its angular frequency in float.
+struct RopeTable {
+  float omega[kPairs];
+  int32_t axis[kPairs];
+};
+
+// Validates a rotary config for head_dim and fills the table (frequencies
+// formed in double, rounded to float).
+h3attn_status make_rope_table(const h3attn_rope_cfg* cfg, int32_t head_dim, RopeTable* out);
+
+// Rows of the packed key workspace per head: each segment starts on a
+// 64-key boundary, at 64 * (ceil(cu[s] / 64) + s).
+inline int64_t packed_rows(int64_t n_tokens, int32_t n_seqs) {
+  return int64_t(kKeyTile) * ((n_tokens + kKeyTile - 1) / kKeyTile + n_seqs);
+}
+
+// Kernel launchers (attn_kernels.hip).  They only enqueue; the caller has
+// validated every argument.  Return hipSuccess or the launch error.
+int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,
+                      const RopeTable& table, void* stream);
+int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const float* pos, int64_t n_tokens,
+                       int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws,
+                       void* v_ws, int64_t rows_per_head, void* stream);
+int launch_attention(const void* q, const int32_t* cu, const float* pos, void* out, float* lse, int64_t n_tokens,
+                     int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
+                     const void* k_ws, const void* v_ws, int64_t rows_per_head, void* stream);
+const char* hip_error_string(int err);
+
+}  // namespace h3attn

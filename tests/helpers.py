@@ -1,0 +1,122 @@
+"""Shared helpers for the GPU parity tests: inputs onto the device, oracle on the host, comparisons."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from joint_sequence_attention_amd import h3attn as H
+from joint_sequence_attention_amd import workloads as wl
+
+# Parity bar for bf16-in / fp32-accumulate attention against the float64 oracle.
+OUT_MAX_ABS = 1e-2
+OUT_MEAN_ABS = 1e-3
+LSE_MAX_ABS = 1e-3
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits_to_device(bits: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def device_to_f64(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return wl.bf16_bits_to_f32(u).astype(np.float64)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def bf16_bits(t) -> np.ndarray:
+    import torch
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+class Case:
+    """One packed batch: layout from the library's host builder, inputs from the seed."""
+
+    def __init__(self, segments, heads, seed, qscale=1.0, device="cuda"):
+        import torch
+        self.segments = segments
+        self.heads = heads
+        self.cu, self.pos = H.h3attn_build_layout(segments)
+        cu_o, pos_o = oracle.layout(segments)
+        assert np.array_equal(self.cu, cu_o) and np.array_equal(self.pos.view(np.uint32), pos_o.view(np.uint32))
+        self.N = int(self.cu[-1])
+        self.lens = np.diff(self.cu.astype(np.int64))
+        self.max_seqlen = int(self.lens.max()) if len(self.lens) else 0
+        self.qb, self.kb, self.vb = wl.random_qkv(self.N, heads, seed, scale=(qscale, 1.0, 1.0))
+        self.q = bits_to_device(self.qb, device)
+        self.k = bits_to_device(self.kb, device)
+        self.v = bits_to_device(self.vb, device)
+        self.cu_d = torch.from_numpy(self.cu).to(device)
+        self.pos_d = torch.from_numpy(np.ascontiguousarray(self.pos)).to(device)
+
+    def run(self, **kw):
+        import torch
+        out, lse = H.h3attn_varlen_fwd(self.q, self.k, self.v, self.cu_d, self.pos_d, self.max_seqlen, **kw)
+        torch.cuda.synchronize()
+        return out, lse
+
+    def oracle_full(self, **kw):
+        return oracle.attention(widen(self.qb), widen(self.kb), widen(self.vb), self.cu, self.pos, **kw)
+
+    def oracle_rows(self, rows, heads=None, **kw):
+        return oracle.attention_rows(widen(self.qb), widen(self.kb), widen(self.vb), self.cu, self.pos, rows, heads,
+                                     **kw)
+
+    def sample_rows(self, n_random=128, seed=0):
+        """Rows that exercise tile edges, segment edges, the audio tail and a random spread."""
+        rng = np.random.default_rng(seed)
+        rows = set()
+        for s in range(len(self.lens)):
+            a, b = int(self.cu[s]), int(self.cu[s + 1])
+            if a == b:
+                continue
+            for off in (0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 257, 511, 512):
+                if a + off < b:
+                    rows.add(a + off)
+            for off in (1, 2, 3, 64, 200, 256):
+                if b - off >= a:
+                    rows.add(b - off)
+        rows.update(int(r) for r in rng.integers(0, self.N, size=n_random))
+        return np.array(sorted(rows), dtype=np.int64)
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, out_max=OUT_MAX_ABS, out_mean=OUT_MEAN_ABS, lse_max=LSE_MAX_ABS,
+            label=""):
+    err = np.abs(out_gpu - out_ref)
+    lerr = np.abs(lse_gpu - lse_ref)
+    stats = dict(out_max=float(err.max()), out_mean=float(err.mean()), lse_max=float(lerr.max()))
+    say(f"{label} parity: out max {stats['out_max']:.3e} mean {stats['out_mean']:.3e} lse max {stats['lse_max']:.3e}")
+    assert np.all(np.isfinite(out_gpu)) and np.all(np.isfinite(lse_gpu))
+    assert stats["out_max"] <= out_max, (label, stats, np.unravel_index(err.argmax(), err.shape))
+    assert stats["out_mean"] <= out_mean, (label, stats)
+    assert stats["lse_max"] <= lse_max, (label, stats, np.unravel_index(lerr.argmax(), lerr.shape))
+    return stats
+
+
+def ragged_segments():
+    """Segment lengths 1, 127, 129, 255, 0, 64, 300, 2 built from grids and audio runs."""
+    return [
+        [wl.visual(1, 1, 1)],
+        [wl.visual(1, 7, 17), wl.audio(8, 1, attached=True)],
+        [wl.visual(2, 8, 8), wl.audio(1, 2, attached=True)],
+        [wl.visual(3, 9, 9), wl.audio(12, 3, attached=True, rule="round")],
+        [],
+        [wl.visual(1, 8, 8)],
+        [wl.visual(2, 10, 14), wl.audio(20, 2, attached=True)],
+        [wl.audio(2, 1.0, attached=False)],
+    ]

@@ -1,0 +1,198 @@
+"""Host-side tests of the C ABI (no GPU needed): exports, layout builder, argument checks.
+
+The layout builder is compared bit for bit with the oracle's layout; the
+argument checks are exercised through ctypes with raw pointers and must return
+their status before anything is launched.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from joint_sequence_attention_amd import h3attn as H
+from joint_sequence_attention_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(H.library_path()):
+        from joint_sequence_attention_amd import build
+        build.build()
+    return H.lib()
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "h3attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3attn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _header_functions()
+    assert declared == sorted(H.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert H.h3attn_abi_version() == 1
+
+
+def test_status_strings(L):
+    assert H.h3attn_status_string(0) == "H3ATTN_OK"
+    assert H.h3attn_status_string(3) == "H3ATTN_ERR_WORKSPACE"
+    assert H.h3attn_status_string(99) == "H3ATTN_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
+def test_layout_bit_exact_vs_oracle(L, name):
+    segs = wl.config(name)["segments"]
+    cu, pos = H.h3attn_build_layout(segs)
+    cu_o, pos_o = oracle.layout(segs)
+    assert cu.dtype == np.int32 and pos.dtype == np.float32
+    assert np.array_equal(cu, cu_o)
+    assert pos.shape == pos_o.shape
+    assert np.array_equal(pos.view(np.uint32), pos_o.view(np.uint32))
+
+
+def test_layout_edge_cases_bit_exact(L):
+    segs = [
+        [wl.visual(1, 1, 1)],
+        [],
+        [wl.visual(2, 3, 5), wl.audio(7, 2, attached=True), wl.audio(5, 1.5, attached=False, rule="round"),
+         wl.audio(0, 3, attached=False), wl.visual(1, 2, 2), wl.audio(3, 1, attached=True, rule="round")],
+        [wl.audio(9, 2.25, attached=False)],
+    ]
+    cu, pos = H.h3attn_build_layout(segs)
+    cu_o, pos_o = oracle.layout(segs)
+    assert np.array_equal(cu, cu_o)
+    assert np.array_equal(pos.view(np.uint32), pos_o.view(np.uint32))
+
+
+def _item(kind, T=1, Hh=1, W=1, n=0, attached=0, rule=0, span=0.0):
+    return H.Item(kind, T, Hh, W, n, attached, rule, 0, span)
+
+
+def _layout_status(L, items, counts):
+    arr = (H.Item * max(1, len(items)))(*items)
+    cnt = (ctypes.c_int32 * max(1, len(counts)))(*counts)
+    n = ctypes.c_int64(-1)
+    return L.h3attn_build_layout(arr, cnt, len(counts), None, None, 0, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize(
+    "items,counts",
+    [
+        ([_item(0, T=0)], [1]),                                  # empty grid
+        ([_item(0, W=-2)], [1]),
+        ([_item(1, n=-1, span=1.0)], [1]),                       # negative audio rows
+        ([_item(1, n=4, span=float("nan"))], [1]),
+        ([_item(1, n=4, span=-1.0)], [1]),
+        ([_item(1, n=4, span=1.0, attached=1)], [1]),            # attached audio without a video
+        ([_item(1, n=4, span=1.0, rule=7)], [1]),
+        ([_item(5)], [1]),                                       # unknown kind
+        ([_item(0)], [-1]),
+        ([_item(0, T=2048, Hh=2048, W=1024)], [1]),              # more than INT32_MAX tokens
+    ],
+)
+def test_layout_rejects_malformed_items(L, items, counts):
+    st, _ = _layout_status(L, items, counts)
+    assert st == H.H3ATTN_ERR_INVALID_ARG
+    assert H.h3attn_last_error() != ""
+
+
+def test_layout_capacity_checked(L):
+    arr = (H.Item * 1)(_item(0, T=2, Hh=2, W=2))
+    cnt = (ctypes.c_int32 * 1)(1)
+    n = ctypes.c_int64(0)
+    buf = (ctypes.c_float * 3)()
+    st = L.h3attn_build_layout(arr, cnt, 1, None, buf, 1, ctypes.byref(n))
+    assert st == H.H3ATTN_ERR_INVALID_ARG and n.value == 8
+    assert L.h3attn_build_layout(arr, cnt, 0, None, None, 0, ctypes.byref(n)) == H.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_build_layout(arr, cnt, 1, None, None, 0, None) == H.H3ATTN_ERR_INVALID_ARG
+
+
+FAKE = 0x10000  # host-side stand-in address; the checks below fail before any launch
+
+
+def _cfg(theta=10000.0, dims=(32, 48, 48)):
+    return ctypes.byref(H.rope_cfg(theta, dims))
+
+
+def _fwd(L, q=FAKE, k=FAKE * 2, v=FAKE * 3, cu=FAKE * 4, pos=FAKE * 5, out=1 << 40, lse=1 << 41, N=64, Hh=2,
+         Dh=128, ns=1, ms=64, scale=0.0, cfg=None, ws=1 << 42, wsb=None):
+    if wsb is None:
+        wsb = L.h3attn_varlen_fwd_workspace_size(N, Hh, 128, ns)
+    return L.h3attn_varlen_fwd(q, k, v, cu, pos, out, lse, N, Hh, Dh, ns, ms, scale, cfg or _cfg(), ws, wsb, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(Dh=64), H.H3ATTN_ERR_UNSUPPORTED),
+        (dict(Dh=256), H.H3ATTN_ERR_UNSUPPORTED),
+        (dict(Hh=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(N=-1), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(ns=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(ms=-1), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(ms=65), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(q=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(k=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(cu=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(pos=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(out=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(lse=0), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("nan")), H.H3ATTN_ERR_INVALID_ARG),
+        (dict(ws=0), H.H3ATTN_ERR_WORKSPACE),
+        (dict(ws=(1 << 42) + 8), H.H3ATTN_ERR_WORKSPACE),
+        (dict(wsb=1024), H.H3ATTN_ERR_WORKSPACE),
+        (dict(out=FAKE), H.H3ATTN_ERR_INVALID_ARG),          # out overlaps q
+        (dict(lse=(1 << 40) + 64), H.H3ATTN_ERR_INVALID_ARG),  # lse overlaps out
+    ],
+)
+def test_varlen_fwd_argument_checks(L, kw, status):
+    assert _fwd(L, **kw) == status
+    assert H.h3attn_last_error() != ""
+
+
+@pytest.mark.parametrize(
+    "dims,theta,status",
+    [
+        ((32, 48, 40), 10000.0, H.H3ATTN_ERR_UNSUPPORTED),   # does not add up to 128
+        ((33, 47, 48), 10000.0, H.H3ATTN_ERR_UNSUPPORTED),   # odd widths
+        ((32, 48, 48), 0.0, H.H3ATTN_ERR_INVALID_ARG),
+        ((32, 48, 48), float("inf"), H.H3ATTN_ERR_INVALID_ARG),
+    ],
+)
+def test_rope_config_checks(L, dims, theta, status):
+    assert _fwd(L, cfg=_cfg(theta, dims)) == status
+    assert L.h3attn_rope_apply(FAKE, FAKE, FAKE * 2, 8, 1, 128, _cfg(theta, dims), None) == status
+
+
+def test_null_rope_config(L):
+    assert L.h3attn_varlen_fwd(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1 << 40, 1 << 41, 8, 1, 128, 1, 8, 0.0,
+                               None, 1 << 42, 1 << 30, None) == H.H3ATTN_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop(L):
+    # N = 0 returns OK without touching any pointer or launching anything
+    assert _fwd(L, q=0, k=0, v=0, cu=0, pos=0, out=0, lse=0, N=0, ms=0, ws=0, wsb=0) == H.H3ATTN_OK
+    assert L.h3attn_rope_apply(None, None, None, 0, 1, 128, _cfg(), None) == H.H3ATTN_OK
+
+
+def test_rope_apply_argument_checks(L):
+    assert L.h3attn_rope_apply(FAKE, FAKE, FAKE * 8, 8, 1, 64, _cfg(), None) == H.H3ATTN_ERR_UNSUPPORTED
+    assert L.h3attn_rope_apply(0, FAKE, FAKE * 8, 8, 1, 128, _cfg(), None) == H.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_apply(FAKE, FAKE + 16, FAKE * 8, 8, 1, 128, _cfg(), None) == H.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_rope_apply(FAKE, FAKE, FAKE * 8, -1, 1, 128, _cfg(), None) == H.H3ATTN_ERR_INVALID_ARG
+
+
+def test_workspace_size_formula(L):
+    # per head: 64 * (ceil(N / 64) + n_seqs) rows of 128 bf16, for keys and for values
+    for N, Hh, ns in [(1, 1, 1), (64, 2, 1), (65, 3, 4), (130048, 5, 1), (45760, 16, 4)]:
+        rows = 64 * ((N + 63) // 64 + ns)
+        assert L.h3attn_varlen_fwd_workspace_size(N, Hh, 128, ns) == 2 * Hh * rows * 128 * 2
+    assert L.h3attn_varlen_fwd_workspace_size(10, 1, 64, 1) == 0

@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bar (floating point, bf16 in / fp32 accumulate): out max-abs <= 1e-2 and
+mean-abs <= 1e-3, lse max-abs <= 1e-3; layout and positions bit-exact (checked
+in every Case); standalone RoPE within 1 bf16 ulp of the rounded oracle.
+Small cases are compared element by element in full; the five workloads are
+compared on sampled rows (every head) in the launch configuration the bench
+times, plus properties over every output (finite values).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import Case, bf16_bits, compare, device_to_f64, ragged_segments, say, widen
+from joint_sequence_attention_amd import h3attn as H
+from joint_sequence_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _ordered(bits):
+    """bf16 bit patterns -> integers that are monotone in the value."""
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _round_bf16_f64(x):
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("name", ["tiny", "480p", "packed", "ref2va"])
+def test_rope_apply_within_one_ulp(gpu, name):
+    cfg = wl.config(name)
+    c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
+    say(f"rope_apply {name}: N={c.N} H={c.heads}")
+    y = H.h3attn_rope_apply(c.q, c.pos_d)
+    ref = oracle.rope(widen(c.qb), c.pos)
+    d = np.abs(_ordered(bf16_bits(y)) - _ordered(_round_bf16_f64(ref)))
+    say(f"rope_apply {name}: max ulp distance {int(d.max())}, share off by one {float((d > 0).mean()):.2e}")
+    assert d.max() <= 1
+
+
+def test_rope_apply_in_place_matches_out_of_place(gpu):
+    cfg = wl.config("480p")
+    c = Case(cfg["segments"], cfg["heads"], 7)
+    y = H.h3attn_rope_apply(c.q, c.pos_d)
+    x = c.q.clone()
+    H.h3attn_rope_apply(x, c.pos_d, out=x)
+    assert np.array_equal(bf16_bits(x), bf16_bits(y))
+
+
+@pytest.mark.parametrize("seed", [1, 1001])
+def test_tiny_full(gpu, seed):
+    cfg = wl.config("tiny")
+    c = Case(cfg["segments"], cfg["heads"], seed)
+    say(f"varlen tiny seed {seed}: N={c.N} H={c.heads}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label=f"tiny/{seed}")
+
+
+@pytest.mark.parametrize("heads", [1, 3])
+def test_ragged_segments_full(gpu, heads):
+    c = Case(ragged_segments(), heads, 40 + heads)
+    say(f"varlen ragged: lens={c.lens.tolist()} H={heads}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="ragged")
+
+
+def test_peaky_softmax_full(gpu):
+    # q scaled by 4: scores spread ~4x wider, so the softmax concentrates on few
+    # keys.  bf16 rounding of the rotated q and k (relative 2^-9 each) then moves
+    # a score by ~|z| * 2^-8 ~ 1.5e-2 at the top of the range, and lse and out
+    # follow the top scores: bound 5e-2 max, 5e-3 mean (lse 5e-2).
+    c = Case(ragged_segments(), 2, 50, qscale=4.0)
+    say(f"varlen peaky: lens={c.lens.tolist()}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, out_max=5e-2, out_mean=5e-3, lse_max=5e-2,
+            label="peaky")
+
+
+@pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va"])
+@pytest.mark.parametrize("seed_offset", [0, wl.ROBUSTNESS_SEED_OFFSET])
+def test_workload_sampled_rows(gpu, name, seed_offset):
+    cfg = wl.config(name)
+    seed = cfg["seed"] + seed_offset
+    c = Case(cfg["segments"], cfg["heads"], seed)
+    say(f"varlen {name} seed {seed}: N={c.N} H={c.heads} segments={len(c.lens)}")
+    out, lse = c.run()
+    out64 = device_to_f64(out)
+    lse64 = device_to_f64(lse)
+    assert np.all(np.isfinite(out64)) and np.all(np.isfinite(lse64))
+    rows = c.sample_rows(n_random=96 if c.N > 100000 else 160, seed=seed)
+    o_ref, l_ref = c.oracle_rows(rows)
+    compare(out64[rows], lse64[:, rows], o_ref, l_ref, label=f"{name}/{seed} ({len(rows)} rows)")
+
+
+def test_fused_rope_equals_standalone_rope(gpu):
+    # Rotating q and k with h3attn_rope_apply and then attending with all
+    # positions zero (rotation by zero is exact) must give bit-identical results.
+    c = Case(ragged_segments(), 2, 60)
+    out, lse = c.run()
+    qr = H.h3attn_rope_apply(c.q, c.pos_d)
+    kr = H.h3attn_rope_apply(c.k, c.pos_d)
+    zero = c.pos_d.clone().zero_()
+    out2, lse2 = H.h3attn_varlen_fwd(qr, kr, c.v, c.cu_d, zero, c.max_seqlen)
+    import torch
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), bf16_bits(out2))
+    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+
+
+def test_two_stages_equal_fused_call(gpu):
+    import torch
+    c = Case(ragged_segments(), 3, 61)
+    out, lse = c.run()
+    ws = H.alloc_workspace(c.N, 3, len(c.lens))
+    H.h3attn_varlen_kv_prologue(c.k, c.v, c.cu_d, c.pos_d, c.max_seqlen, ws)
+    out2, lse2 = H.h3attn_varlen_attention(c.q, c.cu_d, c.pos_d, c.max_seqlen, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), bf16_bits(out2))
+    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+
+
+def test_deterministic(gpu):
+    c = Case(ragged_segments(), 2, 62)
+    o1, l1 = c.run()
+    o2, l2 = c.run()
+    assert np.array_equal(bf16_bits(o1), bf16_bits(o2))
+    assert np.array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+
+
+def test_segment_isolation_bitwise(gpu):
+    # Each packed segment's rows equal a run of that segment alone.
+    import torch
+    cfg = wl.config("packed")
+    segs = [[wl.visual(T, 6, 10), wl.audio(32 * T // 4, T, attached=True)] for T in (3, 5, 2)]
+    c = Case(segs, 2, 63)
+    out, lse = c.run()
+    for s in range(len(segs)):
+        a, b = int(c.cu[s]), int(c.cu[s + 1])
+        cu1 = torch.tensor([0, b - a], dtype=torch.int32, device="cuda")
+        o1, l1 = H.h3attn_varlen_fwd(c.q[a:b].contiguous(), c.k[a:b].contiguous(), c.v[a:b].contiguous(), cu1,
+                                     c.pos_d[a:b].contiguous(), b - a)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(out[a:b]), bf16_bits(o1))
+        assert np.array_equal(lse[:, a:b].cpu().numpy(), l1.cpu().numpy())
+
+
+def test_explicit_scale_and_rope_config(gpu):
+    c = Case(ragged_segments(), 2, 64)
+    out, lse = c.run(softmax_scale=0.05, theta=500.0, dims=(64, 32, 32))
+    o_ref, l_ref = c.oracle_full(scale=0.05, theta=500.0, dims=(64, 32, 32))
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="scale/theta")
+
+
+def test_generous_max_seqlen_and_empty_segments(gpu):
+    import torch
+    segs = [[], [wl.visual(1, 5, 7)], [], [wl.visual(1, 1, 3)], []]
+    c = Case(segs, 2, 65)
+    out, lse = H.h3attn_varlen_fwd(c.q, c.k, c.v, c.cu_d, c.pos_d, c.N)  # max_seqlen = N >= every segment
+    torch.cuda.synchronize()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="empty segments")
+
+
+def test_length_one_segment_returns_v(gpu):
+    c = Case([[wl.visual(1, 1, 1)], [wl.audio(1, 1.0, attached=False)]], 4, 66)
+    out, lse = c.run()
+    assert np.array_equal(bf16_bits(out), c.vb)
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="length-1")
+
+
+def test_zero_tokens_noop(gpu):
+    import torch
+    q = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(2, dtype=torch.int32, device="cuda")
+    pos = torch.empty((0, 3), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out, lse = H.h3attn_varlen_fwd(q, q, q, cu, pos, 0, workspace=ws)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 128) and lse.shape == (2, 0)
+
+
+def test_reordered_references_change_output(gpu):
+    # A different reference order moves positions on the shared clock, which
+    # must show in the attention output beyond the parity tolerance.
+    seg = [wl.visual(1, 4, 6), wl.visual(1, 4, 6), wl.visual(2, 4, 6), wl.audio(16, 2, attached=True)]
+    swapped = [seg[2], seg[3], seg[0], seg[1]]
+    c1 = Case([seg], 2, 67)
+    c2 = Case([swapped], 2, 67)
+    o1, _ = c1.run()
+    o2, _ = c2.run()
+    # same token values, different positions: outputs differ by far more than 1e-2 somewhere
+    assert np.abs(device_to_f64(o1) - device_to_f64(o2)).max() > 5e-2
