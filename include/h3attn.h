@@ -130,8 +130,14 @@ h3attn_status h3attn_rope_apply(const void* x, void* y, const float* pos_thw, in
  * overlap any input.
  *
  * The workspace (device, >= h3attn_varlen_fwd_workspace_size bytes, 256-byte
- * aligned) holds the rotated keys and the transposed values in the layout the
- * attention kernel reads; its contents on return are unspecified.
+ * aligned) holds the rotated keys (fp16, each 64-key tile scaled by a power
+ * of two), the transposed values and the per-tile key scales, in the layout
+ * the attention kernel reads; its contents on return are unspecified.
+ *
+ * Precision: the rotated queries and keys enter the score contraction as
+ * fp16 with power-of-two block scales (one per query row, one per 64-key
+ * tile), which keeps bf16's range; probabilities and values enter the second
+ * contraction as bf16; all accumulation is fp32.
  * ------------------------------------------------------------------- */
 size_t h3attn_varlen_fwd_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs);
 

@@ -67,8 +67,7 @@ h3attn_status check_varlen(int64_t n_tokens, int32_t n_heads, int32_t head_dim, 
 }
 
 size_t workspace_bytes_for(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
-  // rotated keys [H][rows][128] bf16 + transposed values, same size
-  return size_t(2) * size_t(n_heads) * size_t(packed_rows(n_tokens, n_seqs)) * kHeadDim * 2;
+  return workspace_layout(n_tokens, n_heads, n_seqs).total;
 }
 
 h3attn_status check_workspace(const void* ws, size_t bytes, int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
@@ -152,11 +151,11 @@ h3attn_status h3attn_varlen_kv_prologue(const void* k, const void* v, const int3
     st = check_workspace(workspace, workspace_bytes, n_tokens, n_heads, n_seqs);
     if (st != H3ATTN_OK) return st;
     const int64_t rows = packed_rows(n_tokens, n_seqs);
+    const WorkspaceLayout wl = workspace_layout(n_tokens, n_heads, n_seqs);
     char* ws = static_cast<char*>(workspace);
-    void* k_ws = ws;
-    void* v_ws = ws + size_t(n_heads) * rows * kHeadDim * 2;
     return hip_status(launch_kv_prologue(k, v, cu_seqlens, pos_thw, n_tokens, n_heads, n_seqs, max_seqlen, table,
-                                         k_ws, v_ws, rows, stream));
+                                         ws + wl.keys_offset, ws + wl.values_offset,
+                                         reinterpret_cast<float*>(ws + wl.scales_offset), rows, stream));
   } catch (...) {
     return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_kv_prologue");
   }
@@ -187,11 +186,11 @@ h3attn_status h3attn_varlen_attention(const void* q, const int32_t* cu_seqlens, 
       return fail(H3ATTN_ERR_INVALID_ARG, "out and lse must not overlap q, each other or the workspace");
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
     const int64_t rows = packed_rows(n_tokens, n_seqs);
+    const WorkspaceLayout wl = workspace_layout(n_tokens, n_heads, n_seqs);
     const char* ws = static_cast<const char*>(workspace);
-    const void* k_ws = ws;
-    const void* v_ws = ws + size_t(n_heads) * rows * kHeadDim * 2;
     return hip_status(launch_attention(q, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, n_seqs, max_seqlen, scale,
-                                       table, k_ws, v_ws, rows, stream));
+                                       table, ws + wl.keys_offset, ws + wl.values_offset,
+                                       reinterpret_cast<const float*>(ws + wl.scales_offset), rows, stream));
   } catch (...) {
     return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_attention");
   }

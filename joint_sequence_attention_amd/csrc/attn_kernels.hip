@@ -29,6 +29,15 @@
 // The prologue stores V^T with its keys permuted inside each 16-key group so
 // that the matching A operand (8 keys of one value dim) is one contiguous
 // 16-byte LDS read.
+//
+// Operand precision.  The rotated queries and keys feed the score contraction
+// as fp16 with power-of-two block scales: each query row and each 64-key tile
+// is scaled so its largest magnitude lands in [2^14, 2^15) before rounding.
+// That keeps bf16's range with fp16's 11-bit significand (8x finer rounding
+// than bf16; bf16 operands alone put the log-sum-exp off by up to ~1.1e-3 on
+// short sequences).  The two scales multiply into the one coefficient that
+// already turns raw scores into base-2 logits, so the inner loop pays nothing
+// for them.  P and V stay bf16 for the second contraction.
 
 #include <hip/hip_runtime.h>
 
@@ -42,6 +51,8 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
@@ -60,6 +71,45 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   v[0] = static_cast<__bf16>(a);
   v[1] = static_cast<__bf16>(b);
   return __builtin_bit_cast(unsigned, v);
+}
+
+// Two floats -> two fp16 (round to nearest even), low half first.
+__device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
+  f16x2 v;
+  v[0] = static_cast<_Float16>(a);
+  v[1] = static_cast<_Float16>(b);
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// 8 floats times a power of two -> 8 fp16.
+__device__ __forceinline__ u32x4 pack8_f16(const float (&f)[8], float mul) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_f16x2(f[2 * i] * mul, f[2 * i + 1] * mul);
+  return v;
+}
+
+// Power-of-two block scale: with amax = max |x| over a block, returns
+// down = 2^-e and up = 2^e such that amax * down lies in [2^14, 2^15), with
+// e >= -110 so that both factors stay normal floats.  amax = 0 (or not
+// finite) gives 1 and 1.
+__device__ __forceinline__ void block_scale(float amax, float& down, float& up) {
+  if (!(amax > 0.0f) || !__builtin_isfinite(amax)) {
+    down = 1.0f;
+    up = 1.0f;
+    return;
+  }
+  int E;
+  (void)frexpf(amax, &E);  // amax = f * 2^E, f in [0.5, 1)
+  const int e = max(E - 15, -110);
+  down = ldexpf(1.0f, -e);
+  up = ldexpf(1.0f, e);
+}
+
+__device__ __forceinline__ float amax8(const float (&f)[8], float m) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  return m;
 }
 
 __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
@@ -132,7 +182,9 @@ __device__ __forceinline__ int64_t packed_start(int32_t seg_begin, int32_t s) {
 
 // ---------------------------------------------------------------------------
 // K/V prologue.  grid = (key tiles of the longest segment, segments, heads).
-// k_ws: [H][rows][128] rotated keys (rows past a segment's end are zero).
+// k_ws: [H][rows][128] rotated keys as fp16, each 64-key tile scaled by a
+//       power of two (rows past a segment's end are zero).
+// k_scale: [H][rows/64] the factor that undoes each tile's scaling.
 // v_ws: [H][rows/64][128][64] transposed value tiles; inside each 16-key
 //       group the 4-key runs are stored in the order 0, 2, 1, 3.
 // ---------------------------------------------------------------------------
@@ -140,9 +192,11 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
                                                           const int32_t* __restrict__ cu,
                                                           const float* __restrict__ pos, int32_t n_heads,
                                                           RopeTable tab, u32x4* __restrict__ k_ws,
-                                                          u32x2* __restrict__ v_ws, int64_t rows_per_head) {
+                                                          u32x2* __restrict__ v_ws, float* __restrict__ k_scale,
+                                                          int64_t rows_per_head) {
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
+  __shared__ float s_red[4];
   const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const int32_t seg_a = cu[s];
   const int32_t S = cu[s + 1] - seg_a;
@@ -153,20 +207,37 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
   const int64_t prow = packed_start(seg_a, s) + int64_t(tile) * BK;  // packed row of this tile's key 0
 
   // Keys: 1024 chunks, 4 per thread; chunk c is row c / 16, dims 8 * (c % 16) ..
+  // Rotate in fp32, find the tile's largest magnitude, then store fp16 scaled
+  // by the tile's power-of-two factor (and the factor itself).
+  float kf[4][8];
+  float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + 256 * i;
     const int r = c >> 4, cc = c & 15;
     const int key = tile * BK + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
     if (key < S) {
       const int64_t tok = int64_t(seg_a) + key;
-      float f[8];
-      unpack8(k[(tok * n_heads + h) * CHUNKS_PER_ROW + cc], f);
-      rope8(f, cc * 4, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
-      val = pack8(f);
+      unpack8(k[(tok * n_heads + h) * CHUNKS_PER_ROW + cc], kf[i]);
+      rope8(kf[i], cc * 4, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[i][e] = 0.0f;
     }
-    k_ws[(int64_t(h) * rows_per_head + prow + r) * CHUNKS_PER_ROW + cc] = val;
+    amax = amax8(kf[i], amax);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float down, up;
+  block_scale(amax, down, up);
+  if (tid == 0) k_scale[int64_t(h) * (rows_per_head / BK) + prow / BK] = up;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    k_ws[(int64_t(h) * rows_per_head + prow + (c >> 4)) * CHUNKS_PER_ROW + (c & 15)] = pack8_f16(kf[i], down);
   }
 
   // Values: thread owns keys 4*k4 .. 4*k4+3 and dims 8*dc .. 8*dc+7.
@@ -227,9 +298,10 @@ template <int NW, int QB>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restrict__ q, const int32_t* __restrict__ cu,
                                                            const float* __restrict__ pos, u32x2* __restrict__ out,
                                                            float* __restrict__ lse, int32_t n_tokens, int32_t n_heads,
-                                                           float scale, float scale_log2, RopeTable tab,
+                                                           float scale_log2, RopeTable tab,
                                                            const u32x4* __restrict__ k_ws,
-                                                           const u32x4* __restrict__ v_ws, int64_t rows_per_head) {
+                                                           const u32x4* __restrict__ v_ws,
+                                                           const float* __restrict__ k_scale, int64_t rows_per_head) {
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * QB * 32;
   constexpr int CH = TILE_CHUNKS / NT;  // chunks per thread per tensor per tile
@@ -251,6 +323,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
   const int64_t prow = packed_start(seg_a, s);
   const u32x4* kg = k_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
   const u32x4* vg = v_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
+  const float* ksc = k_scale + int64_t(h) * (rows_per_head / BK) + prow / BK;
 
   // First key/value tile: issue the loads before the query rotation.
   u32x4 kreg[CH], vreg[CH];
@@ -262,28 +335,41 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
   __syncthreads();  // rope table staged
 
   // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 of block qb
-  // and dims 16*ks + 8*g .. +7 for ks = 0..7, rotated and rounded to bf16.
-  bf16x8 qf[QB][8];
+  // and dims 16*ks + 8*g .. +7 for ks = 0..7, rotated in fp32, then scaled by
+  // the row's power-of-two factor and rounded to fp16.  cq folds the undoing
+  // factor into the base-2 logit coefficient.
+  f16x8 qf[QB][8];
+  float cq[QB];
   int qrow[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int r = qt * BQ + (wave * QB + qb) * 32 + l32;
     qrow[qb] = r;
+    float f[8][8];
     if (r < S) {
       const int64_t tok = int64_t(seg_a) + r;
       const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
       const u32x4* qp = q + (tok * n_heads + h) * CHUNKS_PER_ROW;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        float f[8];
-        unpack8(qp[2 * ks + g], f);
-        rope8(f, ks * 8 + g * 4, s_omega, s_axis, pt, ph, pw);
-        qf[qb][ks] = __builtin_bit_cast(bf16x8, pack8(f));
+        unpack8(qp[2 * ks + g], f[ks]);
+        rope8(f[ks], ks * 8 + g * 4, s_omega, s_axis, pt, ph, pw);
       }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[ks][e] = 0.0f;
     }
+    float amax = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) amax = amax8(f[ks], amax);
+    amax = pair_max(amax);  // the row's other 64 dims sit in lane L ^ 32
+    float down, up;
+    block_scale(amax, down, up);
+    cq[qb] = scale_log2 * up;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = __builtin_bit_cast(f16x8, pack8_f16(f[ks], down));
   }
 
   auto store_stage = [&](int stage) {
@@ -337,10 +423,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sk + ((32 * sb + l32) * KSTR + 16 * ks + 8 * g) * 2);
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(sk + ((32 * sb + l32) * KSTR + 16 * ks + 8 * g) * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sacc[sb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sacc[sb][qb], 0, 0, 0);
+          sacc[sb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], sacc[sb][qb], 0, 0, 0);
       }
     }
 
@@ -359,26 +445,29 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
         }
     }
 
-    // Online softmax (base 2, scores kept in raw units; scale folded into the exponent).
+    // Online softmax in base 2.  c turns a raw score of this tile into a
+    // base-2 logit (softmax scale, log2 e and both block scales); m and the
+    // exponents are kept in base-2 logit units.
+    const float kscale_t = ksc[kt];
     bf16x8 pf[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      const float c = cq[qb] * kscale_t;
       float mx = sacc[0][qb][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][qb][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][qb][r]);
       mx = pair_max(mx);
-      const float m_new = fmaxf(m[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_new) * scale_log2);
+      const float m_new = fmaxf(m[qb], mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
       m[qb] = m_new;
-      const float mc = m_new * scale_log2;
       float rs = 0.0f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][r], scale_log2, -mc));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][r], c, -m_new));
           sacc[sb][qb][r] = p;
           rs += p;
         }
@@ -416,7 +505,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
     __syncthreads();
   }
 
-  // Epilogue: O = O / l, lse = scale * m + ln l.
+  // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = pair_sum(l[qb]);
@@ -433,7 +522,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
           w[1] = pack_bf16x2(o[qb][db][4 * k4 + 2] * inv, o[qb][db][4 * k4 + 3] * inv);
           orow[db * 8 + 2 * k4 + g] = w;
         }
-      if (g == 0) lse[int64_t(h) * n_tokens + tok] = fmaf(m[qb], scale, logf(lt));
+      if (g == 0) lse[int64_t(h) * n_tokens + tok] = (m[qb] + log2f(lt)) * 0.69314718055994531f;
     }
   }
 }
@@ -460,18 +549,19 @@ int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens
 
 int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const float* pos, int64_t /*n_tokens*/,
                        int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws,
-                       void* v_ws, int64_t rows_per_head, void* stream) {
+                       void* v_ws, float* k_scale, int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + BK - 1) / BK);
   if (tiles == 0) return 0;
   hipLaunchKernelGGL(kv_prologue_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), cu,
-                     pos, n_heads, table, static_cast<u32x4*>(k_ws), static_cast<u32x2*>(v_ws), rows_per_head);
+                     pos, n_heads, table, static_cast<u32x4*>(k_ws), static_cast<u32x2*>(v_ws), k_scale,
+                     rows_per_head);
   return int(hipGetLastError());
 }
 
 int launch_attention(const void* q, const int32_t* cu, const float* pos, void* out, float* lse, int64_t n_tokens,
                      int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
-                     const void* k_ws, const void* v_ws, int64_t rows_per_head, void* stream) {
+                     const void* k_ws, const void* v_ws, const float* k_scale, int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + ATTN_BQ - 1) / ATTN_BQ);
   if (tiles == 0) return 0;
   static bool attr_set = false;
@@ -484,8 +574,8 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL((attn_fwd_kernel<ATTN_NW, ATTN_QB>), dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),
                      dim3(ATTN_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
-                     pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale, scale_log2, table,
-                     static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), rows_per_head);
+                     pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
+                     static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), k_scale, rows_per_head);
   return int(hipGetLastError());
 }
 

@@ -33,16 +33,35 @@ inline int64_t packed_rows(int64_t n_tokens, int32_t n_seqs) {
   return int64_t(kKeyTile) * ((n_tokens + kKeyTile - 1) / kKeyTile + n_seqs);
 }
 
+// Workspace layout, in this order:
+//   keys    fp16 [H][rows][128]     rotated, each 64-key tile block-scaled
+//   values  bf16 [H][rows/64][128][64]  transposed tiles
+//   scales  fp32 [H][rows/64]       per-tile factor that undoes the key scaling
+struct WorkspaceLayout {
+  size_t keys_offset, values_offset, scales_offset, total;
+};
+inline WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
+  const size_t rows = size_t(packed_rows(n_tokens, n_seqs));
+  const size_t plane = size_t(n_heads) * rows * kHeadDim * 2;
+  WorkspaceLayout w;
+  w.keys_offset = 0;
+  w.values_offset = plane;
+  w.scales_offset = 2 * plane;
+  w.total = 2 * plane + size_t(n_heads) * (rows / kKeyTile) * 4;
+  return w;
+}
+
 // Kernel launchers (attn_kernels.hip).  They only enqueue; the caller has
 // validated every argument.  Return hipSuccess or the launch error.
 int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,
                       const RopeTable& table, void* stream);
 int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const float* pos, int64_t n_tokens,
                        int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws,
-                       void* v_ws, int64_t rows_per_head, void* stream);
+                       void* v_ws, float* k_scale, int64_t rows_per_head, void* stream);
 int launch_attention(const void* q, const int32_t* cu, const float* pos, void* out, float* lse, int64_t n_tokens,
                      int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
-                     const void* k_ws, const void* v_ws, int64_t rows_per_head, void* stream);
+                     const void* k_ws, const void* v_ws, const float* k_scale, int64_t rows_per_head,
+                     void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace h3attn

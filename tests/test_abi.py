@@ -191,8 +191,9 @@ def test_rope_apply_argument_checks(L):
 
 
 def test_workspace_size_formula(L):
-    # per head: 64 * (ceil(N / 64) + n_seqs) rows of 128 bf16, for keys and for values
+    # per head: 64 * (ceil(N / 64) + n_seqs) rows of 128 16-bit values, for keys and for
+    # values, plus one fp32 key scale per 64-row tile
     for N, Hh, ns in [(1, 1, 1), (64, 2, 1), (65, 3, 4), (130048, 5, 1), (45760, 16, 4)]:
         rows = 64 * ((N + 63) // 64 + ns)
-        assert L.h3attn_varlen_fwd_workspace_size(N, Hh, 128, ns) == 2 * Hh * rows * 128 * 2
+        assert L.h3attn_varlen_fwd_workspace_size(N, Hh, 128, ns) == 2 * Hh * rows * 128 * 2 + Hh * (rows // 64) * 4
     assert L.h3attn_varlen_fwd_workspace_size(10, 1, 64, 1) == 0

@@ -2,7 +2,8 @@
 
 Bar (floating point, bf16 in / fp32 accumulate): out max-abs <= 1e-2 and
 mean-abs <= 1e-3, lse max-abs <= 1e-3; layout and positions bit-exact (checked
-in every Case); standalone RoPE within 1 bf16 ulp of the rounded oracle.
+in every Case); standalone RoPE within one bf16 ulp plus the fp32 arithmetic's
+own error bound (see _rope_bound).
 Small cases are compared element by element in full; the five workloads are
 compared on sampled rows (every head) in the launch configuration the bench
 times, plus properties over every output (finite values).
@@ -33,16 +34,46 @@ def _round_bf16_f64(x):
     return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
 
 
+def _rope_bound(x, pos, dims=(32, 48, 48), theta=10000.0):
+    """Per-element error bound for an fp32 rotation rounded to bf16.
+
+    One bf16 ulp of the exact value for the final rounding, plus the fp32
+    arithmetic before it: the frequency and the angle phi = p * omega are each
+    rounded to fp32 (angle error <= |phi| 2^-23), sincos and the multiply-adds
+    add a few 2^-24 relative to the pair's inputs.  Bound on that part:
+    2^-22 (1 + |phi|) (|x0| + |x1|), which matters only where the rotated value
+    nearly cancels and is far smaller than its inputs.
+    """
+    phis = []
+    for axis, width in enumerate(dims):
+        phis.append(np.asarray(pos, dtype=np.float64)[:, axis][:, None] * oracle.rope_frequencies(theta, width)[None, :])
+    phi = np.concatenate(phis, axis=1)                      # [N, 64]
+    pair = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])      # [N, H, 64]
+    arith = 2.0 ** -22 * (1.0 + np.abs(phi))[:, None, :] * pair
+    return np.repeat(arith, 2, axis=-1)
+
+
+def _bf16_ulp(v):
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
 @pytest.mark.parametrize("name", ["tiny", "480p", "packed", "ref2va"])
-def test_rope_apply_within_one_ulp(gpu, name):
+def test_rope_apply_parity(gpu, name):
     cfg = wl.config(name)
     c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
     say(f"rope_apply {name}: N={c.N} H={c.heads}")
     y = H.h3attn_rope_apply(c.q, c.pos_d)
-    ref = oracle.rope(widen(c.qb), c.pos)
-    d = np.abs(_ordered(bf16_bits(y)) - _ordered(_round_bf16_f64(ref)))
-    say(f"rope_apply {name}: max ulp distance {int(d.max())}, share off by one {float((d > 0).mean()):.2e}")
-    assert d.max() <= 1
+    x = widen(c.qb)
+    ref = oracle.rope(x, c.pos)
+    yb = bf16_bits(y)
+    d = np.abs(_ordered(yb) - _ordered(_round_bf16_f64(ref)))
+    err = np.abs(widen(yb) - ref)
+    bound = _bf16_ulp(ref) + _rope_bound(x, c.pos)
+    say(f"rope_apply {name}: within 1 ulp of the rounded oracle: {float((d <= 1).mean()):.6f}; "
+        f"max err / bound {float((err / bound).max()):.3f}")
+    assert np.all(err <= bound)
+    assert float((d <= 1).mean()) > 0.9999
 
 
 def test_rope_apply_in_place_matches_out_of_place(gpu):
@@ -102,19 +133,21 @@ def test_workload_sampled_rows(gpu, name, seed_offset):
     compare(out64[rows], lse64[:, rows], o_ref, l_ref, label=f"{name}/{seed} ({len(rows)} rows)")
 
 
-def test_fused_rope_equals_standalone_rope(gpu):
+def test_fused_rope_turns_like_standalone_rope(gpu):
     # Rotating q and k with h3attn_rope_apply and then attending with all
-    # positions zero (rotation by zero is exact) must give bit-identical results.
+    # positions zero (a rotation by zero is exact) must agree with the fused
+    # path up to the extra bf16 rounding of the rotated operands (relative
+    # 2^-9 per element; on this case lse moves by < 3e-3 and out by < 1e-2).
+    # A rotation that differed from the standalone one (wrong pair, sign or
+    # frequency) would move scores by O(1).
     c = Case(ragged_segments(), 2, 60)
     out, lse = c.run()
     qr = H.h3attn_rope_apply(c.q, c.pos_d)
     kr = H.h3attn_rope_apply(c.k, c.pos_d)
     zero = c.pos_d.clone().zero_()
     out2, lse2 = H.h3attn_varlen_fwd(qr, kr, c.v, c.cu_d, zero, c.max_seqlen)
-    import torch
-    torch.cuda.synchronize()
-    assert np.array_equal(bf16_bits(out), bf16_bits(out2))
-    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+    compare(device_to_f64(out2), device_to_f64(lse2), device_to_f64(out), device_to_f64(lse), out_max=1e-2,
+            out_mean=1e-3, lse_max=3e-3, label="fused vs standalone rope")
 
 
 def test_two_stages_equal_fused_call(gpu):
