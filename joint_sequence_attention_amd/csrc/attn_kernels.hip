@@ -43,6 +43,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -61,6 +62,9 @@ constexpr int D = kHeadDim;
 constexpr int BK = kKeyTile;                    // keys per tile
 constexpr int CHUNKS_PER_ROW = D / 8;           // 16-byte chunks per 128-dim row
 constexpr int TILE_CHUNKS = BK * CHUNKS_PER_ROW;  // 1024 chunks = 16 KiB per tile
+
+// (1.0, 1.0) as packed bf16, for row sums through v_dot2_f32_bf16.
+#define BF16_ONES (__builtin_bit_cast(bf16x2, 0x3f803f80u))
 
 __device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
@@ -293,6 +297,7 @@ constexpr int VSTR = BK + 8;  // bf16 per V^T row in LDS
 constexpr int K_LDS_BYTES = BK * KSTR * 2;
 constexpr int V_LDS_BYTES = D * VSTR * 2;
 constexpr int STAGE_BYTES = K_LDS_BYTES + V_LDS_BYTES;
+constexpr float RESCALE_SLACK = 8.0f;  // base-2 logit units the running max may lag behind
 
 template <int NW, int QB>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restrict__ q, const int32_t* __restrict__ cu,
@@ -397,21 +402,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
       for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
   }
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // One 64-key tile: S^T, (mask), online softmax, O^T += V^T P^T.
+  // The running maximum m (base-2 logit units) only moves when a tile's
+  // maximum exceeds it by more than RESCALE_SLACK; until then probabilities
+  // are exp2(t - m) <= 2^RESCALE_SLACK, which bf16 and fp32 hold without loss,
+  // and O and l need no rescaling.  The result is exact either way because
+  // the final normalisation divides by an l built with the same m.
+  auto tile_step = [&](int kt, auto masked) {
     const char* sk = smem + (kt & 1) * STAGE_BYTES;
     const char* sv = sk + K_LDS_BYTES;
-    const bool more = kt + 1 < n_kt;
-    if (more) {
-      const u32x4* kn = kg + int64_t(kt + 1) * TILE_CHUNKS;
-      const u32x4* vn = vg + int64_t(kt + 1) * TILE_CHUNKS;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        kreg[i] = kn[tid + i * NT];
-        vreg[i] = vn[tid + i * NT];
-      }
-    }
 
-    // S^T for two 32-key sub-blocks.
     f32x16 sacc[2][QB];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -430,8 +430,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
       }
     }
 
-    // Keys past the segment end (last tile only) get probability zero.
-    if (kt == n_kt - 1 && (S % BK) != 0) {
+    if constexpr (decltype(masked)::value) {
+      // keys past the segment end get probability zero
       const int kbase = kt * BK;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -445,46 +445,60 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
         }
     }
 
-    // Online softmax in base 2.  c turns a raw score of this tile into a
-    // base-2 logit (softmax scale, log2 e and both block scales); m and the
-    // exponents are kept in base-2 logit units.
+    // c turns a raw score of this tile into a base-2 logit (softmax scale,
+    // log2 e and both block scales).
     const float kscale_t = ksc[kt];
-    bf16x8 pf[QB][2][2];
+    float c[QB], tmax[QB];
+    bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float c = cq[qb] * kscale_t;
+      c[qb] = cq[qb] * kscale_t;
       float mx = sacc[0][qb][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][qb][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][qb][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m[qb], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);
-      m[qb] = m_new;
-      float rs = 0.0f;
+      tmax[qb] = pair_max(mx) * c[qb];
+      grow = grow || (tmax[qb] > m[qb] + RESCALE_SLACK);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; rare after the first tile
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = tmax[qb] > m[qb] + RESCALE_SLACK ? tmax[qb] : m[qb];
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);  // 1 where m stays, 0 from -inf
+        m[qb] = m_new;
+        l[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][r], c, -m_new));
-          sacc[sb][qb][r] = p;
-          rs += p;
-        }
-      l[qb] = fmaf(l[qb], alpha, rs);
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+      }
+    }
+
+    bf16x8 pf[QB][2][2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs = l[qb];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          u32x4 w;
+          // Packed into separate scalars first: a v_dot2 whose source is an
+          // element of a 128-bit vector is miscompiled by this toolchain (it
+          // reads element 0 every time).
+          unsigned pk[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(sacc[sb][qb][8 * hh + 2 * i], sacc[sb][qb][8 * hh + 2 * i + 1]);
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][8 * hh + 2 * i], c[qb], -m[qb]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][8 * hh + 2 * i + 1], c[qb], -m[qb]));
+            pk[i] = pack_bf16x2(p0, p1);
+            // row sum of the bf16 probabilities, the same values the PV product uses
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), BF16_ONES, rs, false);
+          }
+          const u32x4 w = {pk[0], pk[1], pk[2], pk[3]};
           pf[qb][sb][hh] = __builtin_bit_cast(bf16x8, w);
         }
+      l[qb] = rs;
     }
 
     // O^T += V^T P^T.
@@ -500,10 +514,22 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
           for (int qb = 0; qb < QB; ++qb)
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][sb][hh], o[qb][db], 0, 0, 0);
         }
+  };
 
-    if (more) store_stage((kt + 1) & 1);
+  // All tiles but the last are full; the last one is masked.
+  for (int kt = 0; kt + 1 < n_kt; ++kt) {
+    const u32x4* kn = kg + int64_t(kt + 1) * TILE_CHUNKS;
+    const u32x4* vn = vg + int64_t(kt + 1) * TILE_CHUNKS;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      kreg[i] = kn[tid + i * NT];
+      vreg[i] = vn[tid + i * NT];
+    }
+    tile_step(kt, std::false_type{});
+    store_stage((kt + 1) & 1);
     __syncthreads();
   }
+  tile_step(n_kt - 1, std::true_type{});
 
   // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
 #pragma unroll
