@@ -62,9 +62,7 @@ constexpr int D = kHeadDim;
 constexpr int BK = kKeyTile;                    // keys per tile
 constexpr int CHUNKS_PER_ROW = D / 8;           // 16-byte chunks per 128-dim row
 constexpr int TILE_CHUNKS = BK * CHUNKS_PER_ROW;  // 1024 chunks = 16 KiB per tile
-
-// (1.0, 1.0) as packed bf16, for row sums through v_dot2_f32_bf16.
-#define BF16_ONES (__builtin_bit_cast(bf16x2, 0x3f803f80u))
+constexpr int VT = 32;                           // keys per transposed value tile
 
 __device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
@@ -189,7 +187,7 @@ __device__ __forceinline__ int64_t packed_start(int32_t seg_begin, int32_t s) {
 // k_ws: [H][rows][128] rotated keys as fp16, each 64-key tile scaled by a
 //       power of two (rows past a segment's end are zero).
 // k_scale: [H][rows/64] the factor that undoes each tile's scaling.
-// v_ws: [H][rows/64][128][64] transposed value tiles; inside each 16-key
+// v_ws: [H][rows/32][128][32] transposed 32-key value tiles; inside each 16-key
 //       group the 4-key runs are stored in the order 0, 2, 1, 3.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
@@ -256,10 +254,11 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[i][j] = val[j];
     }
-    // stored position of this 4-key run inside its 16-key group
-    const int run = k4 & 3;
-    const int kpos = 16 * (k4 >> 2) + 4 * (((run & 1) << 1) | (run >> 1));
-    u32x2* vt = v_ws + (int64_t(h) * (rows_per_head / BK) + prow / BK) * (D * BK / 4);
+    // 32-key value tile this run falls in, and the stored position of the
+    // 4-key run inside its 16-key group
+    const int half = k4 >> 3, run = k4 & 3;
+    const int kpos = 16 * ((k4 & 7) >> 2) + 4 * (((run & 1) << 1) | (run >> 1));
+    u32x2* vt = v_ws + (int64_t(h) * (rows_per_head / VT) + prow / VT + half) * (D * VT / 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // dims 8*dc + 2j (low halves) and 8*dc + 2j + 1 (high halves)
@@ -269,8 +268,8 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
       hi[0] = (w[0][j] >> 16) | (w[1][j] & 0xffff0000u);
       hi[1] = (w[2][j] >> 16) | (w[3][j] & 0xffff0000u);
       const int d = 8 * dc + 2 * j;
-      vt[(d * BK + kpos) / 4] = lo;
-      vt[((d + 1) * BK + kpos) / 4] = hi;
+      vt[(d * VT + kpos) / 4] = lo;
+      vt[((d + 1) * VT + kpos) / 4] = hi;
     }
   }
 }
@@ -288,31 +287,54 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Attention forward.  NW waves per workgroup, each owning QB blocks of 32
-// query rows; BQ = 32 * NW * QB query rows per workgroup.
+// Attention forward.  Eight waves per workgroup, one 32-row query block per
+// wave; BQ = 256 query rows per workgroup.
 // grid = (query tiles of the longest segment, segments, heads).
+//
+// Ping-pong schedule.  Waves 0-3 (group A) and waves 4-7 (group B) land one
+// of each on every SIMD and work through the same 64-key tiles half a phase
+// apart.  Between two barriers, for tile t:
+//   group A:  S(t) = K(t) Q^T  |  softmax(t)    |  O += V(t) P(t)
+//   group B:  softmax(t-1)     |  O += V(t-1) P(t-1)  |  S(t) = K(t) Q^T
+// so while one wave of a SIMD runs its softmax (VALU) the other issues MFMAs.
+// Each wave's own code stays in plain order; the overlap comes from the two
+// waves.  Group B finishes its last tile after the loop.
+//
+// LDS: a ring of two key tiles (16 KiB each) and three value tiles (group B
+// reads value tile t-1 while tile t+1 is being filled), filled by direct
+// global->LDS loads one tile ahead.  Rows are not padded; 16-byte chunks are
+// XOR-swizzled so that every fragment read (16 lanes on 16 different rows,
+// same logical chunk) touches each bank once:
+//   key tile         64 rows x 16 chunks: chunk c of row r at r*256 + 16*(c ^ (r & 15))
+//   value sub-tile  128 rows x  4 chunks: chunk c of row d at d*64 + 16*(c ^ ((d >> 2) & 3))
+// (a 64-key value tile is two 32-key sub-tiles, as in the workspace).
 // ---------------------------------------------------------------------------
-constexpr int KSTR = D + 8;   // bf16 per K row in LDS (16-byte pad against bank conflicts)
-constexpr int VSTR = BK + 8;  // bf16 per V^T row in LDS
-constexpr int K_LDS_BYTES = BK * KSTR * 2;
-constexpr int V_LDS_BYTES = D * VSTR * 2;
-constexpr int STAGE_BYTES = K_LDS_BYTES + V_LDS_BYTES;
+constexpr int KT_BYTES = BK * D * 2;    // 16 KiB key tile
+constexpr int VT_BYTES = BK * D * 2;    // 16 KiB value tile (two sub-tiles of 8 KiB)
+constexpr int KSLOTS = 2, VSLOTS = 3;
 constexpr float RESCALE_SLACK = 8.0f;  // base-2 logit units the running max may lag behind
 
-template <int NW, int QB>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restrict__ q, const int32_t* __restrict__ cu,
-                                                           const float* __restrict__ pos, u32x2* __restrict__ out,
-                                                           float* __restrict__ lse, int32_t n_tokens, int32_t n_heads,
-                                                           float scale_log2, RopeTable tab,
-                                                           const u32x4* __restrict__ k_ws,
-                                                           const u32x4* __restrict__ v_ws,
-                                                           const float* __restrict__ k_scale, int64_t rows_per_head) {
+__device__ __forceinline__ int k_lds_offset(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
+__device__ __forceinline__ int v_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ ((d >> 2) & 3)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int ATTN_NW = 8;
+constexpr int ATTN_BQ = 32 * ATTN_NW;
+constexpr size_t ATTN_SMEM = KSLOTS * KT_BYTES + VSLOTS * VT_BYTES;
+
+__global__ __launch_bounds__(ATTN_NW * 64, 1) void attn_fwd_kernel(
+    const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
+    u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
+    RopeTable tab, const u32x4* __restrict__ k_ws, const u32x4* __restrict__ v_ws, const float* __restrict__ k_scale,
+    int64_t rows_per_head) {
+  constexpr int NW = ATTN_NW;
   constexpr int NT = NW * 64;
-  constexpr int BQ = NW * QB * 32;
-  constexpr int CH = TILE_CHUNKS / NT;  // chunks per thread per tensor per tile
+  constexpr int BQ = ATTN_BQ;
+  constexpr int LOADS = TILE_CHUNKS / NT;  // direct-load instructions per wave per tile and tensor
   static_assert(TILE_CHUNKS % NT == 0, "tile must split evenly over the workgroup");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // 2 stages
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // key slots, then value slots
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
 
@@ -330,29 +352,44 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
   const u32x4* vg = v_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
   const float* ksc = k_scale + int64_t(h) * (rows_per_head / BK) + prow / BK;
 
-  // First key/value tile: issue the loads before the query rotation.
-  u32x4 kreg[CH], vreg[CH];
+  // Lane L of load instruction i fills LDS chunk p = (i*NW + wave)*64 + L of
+  // the tile, so it fetches the logical chunk the swizzle puts there.
+  auto load_tiles = [&](int t) {
+    const u32x4* ksrc = kg + int64_t(t) * TILE_CHUNKS;
+    const u32x4* vsrc = vg + int64_t(t) * TILE_CHUNKS;
+    char* kdst = smem + (t % KSLOTS) * KT_BYTES;
+    char* vdst = smem + KSLOTS * KT_BYTES + (t % VSLOTS) * VT_BYTES;
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    kreg[i] = kg[tid + i * NT];
-    vreg[i] = vg[tid + i * NT];
-  }
+    for (int i = 0; i < LOADS; ++i) {
+      const int p = (i * NW + wave) * 64 + lane;
+      const int r = p >> 4, c = (p & 15) ^ (r & 15);
+      __builtin_amdgcn_global_load_lds(ksrc + r * CHUNKS_PER_ROW + c, (lds_void*)(kdst + (i * NW + wave) * 1024), 16,
+                                       0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int p = (i * NW + wave) * 64 + lane;
+      const int sub = p >> 9, qq = p & 511;
+      const int d = qq >> 2, c = (qq & 3) ^ ((d >> 2) & 3);
+      __builtin_amdgcn_global_load_lds(vsrc + sub * 512 + d * 4 + c, (lds_void*)(vdst + (i * NW + wave) * 1024), 16,
+                                       0, 0);
+    }
+  };
+
+  load_tiles(0);  // first tile loads while the queries are rotated
   __syncthreads();  // rope table staged
 
-  // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 of block qb
-  // and dims 16*ks + 8*g .. +7 for ks = 0..7, rotated in fp32, then scaled by
-  // the row's power-of-two factor and rounded to fp16.  cq folds the undoing
-  // factor into the base-2 logit coefficient.
-  f16x8 qf[QB][8];
-  float cq[QB];
-  int qrow[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = qt * BQ + (wave * QB + qb) * 32 + l32;
-    qrow[qb] = r;
+  // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 of its block
+  // and dims 16*ks + 8*g .. +7, rotated in fp32, scaled by the row's
+  // power-of-two factor and rounded to fp16; cq folds the undoing factor into
+  // the base-2 logit coefficient.
+  f16x8 qf[8];
+  float cq;
+  const int qrow = qt * BQ + wave * 32 + l32;
+  {
     float f[8][8];
-    if (r < S) {
-      const int64_t tok = int64_t(seg_a) + r;
+    if (qrow < S) {
+      const int64_t tok = int64_t(seg_a) + qrow;
       const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
       const u32x4* qp = q + (tok * n_heads + h) * CHUNKS_PER_ROW;
 #pragma unroll
@@ -372,191 +409,179 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const u32x4* __restri
     amax = pair_max(amax);  // the row's other 64 dims sit in lane L ^ 32
     float down, up;
     block_scale(amax, down, up);
-    cq[qb] = scale_log2 * up;
+    cq = scale_log2 * up;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = __builtin_bit_cast(f16x8, pack8_f16(f[ks], down));
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(f16x8, pack8_f16(f[ks], down));
   }
 
-  auto store_stage = [&](int stage) {
-    char* sk = smem + stage * STAGE_BYTES;
-    char* sv = sk + K_LDS_BYTES;
+  // Per-lane fragment offsets within a slot (the sub-block / value-dim
+  // block / sub-tile parts are immediate offsets on top).
+  int koff[8], voff[2];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<u32x4*>(sk + ((c >> 4) * KSTR + (c & 15) * 8) * 2) = kreg[i];
-      *reinterpret_cast<u32x4*>(sv + ((c >> 3) * VSTR + (c & 7) * 8) * 2) = vreg[i];
-    }
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = k_lds_offset(l32, 2 * ks + g);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) voff[hh] = KSLOTS * KT_BYTES + v_lds_offset(l32, 2 * hh + g);
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  f32x16 sc[2];       // S^T of one 64-key tile (two 32-key sub-blocks)
+  bf16x8 pf[2][2];    // its probabilities, [sub-block][key half]
+
+  // Fragment prefetch: LDS reads take longer than an MFMA, so each chain's
+  // operands are read eight ahead and a register is refilled as soon as its
+  // MFMA has been issued.
+  bf16x8 fr[8];
+  auto k_frag = [&](const char* kb, int sb, int ks) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + sb * 32 * 256 + koff[ks]));
   };
-  store_stage(0);
-  __syncthreads();
-
-  f32x16 o[QB][4];
-  float m[QB], l[QB];
+  auto v_frag = [&](const char* vb, int sb, int hh, int db) {
+    return *reinterpret_cast<const bf16x8*>(vb + sb * (VT_BYTES / 2) + db * 32 * 64 + voff[hh]);
+  };
+  // S^T for tile t: 2 sub-blocks x 8 MFMAs over the head dim.
+  auto qk = [&](int t) {
+    const char* kb = smem + (t % KSLOTS) * KT_BYTES;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
-  }
-
-  // One 64-key tile: S^T, (mask), online softmax, O^T += V^T P^T.
-  // The running maximum m (base-2 logit units) only moves when a tile's
-  // maximum exceeds it by more than RESCALE_SLACK; until then probabilities
-  // are exp2(t - m) <= 2^RESCALE_SLACK, which bf16 and fp32 hold without loss,
-  // and O and l need no rescaling.  The result is exact either way because
-  // the final normalisation divides by an l built with the same m.
-  auto tile_step = [&](int kt, auto masked) {
-    const char* sk = smem + (kt & 1) * STAGE_BYTES;
-    const char* sv = sk + K_LDS_BYTES;
-
-    f32x16 sacc[2][QB];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sb][qb][r] = 0.0f;
+    for (int ks = 0; ks < 8; ++ks) fr[ks] = k_frag(kb, 0, ks);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
+      for (int r = 0; r < 16; ++r) sc[sb][r] = 0.0f;
+#pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(sk + ((32 * sb + l32) * KSTR + 16 * ks + 8 * g) * 2);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[sb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], sacc[sb][qb], 0, 0, 0);
+        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fr[ks]), qf[ks], sc[sb], 0, 0, 0);
+        if (sb == 0) fr[ks] = k_frag(kb, 1, ks);
       }
     }
-
-    if constexpr (decltype(masked)::value) {
-      // keys past the segment end get probability zero
-      const int kbase = kt * BK;
+  };
+  // First eight value fragments of tile t (sub-block 0), read ahead of the
+  // softmax so they arrive while it runs.
+  auto pv_prefetch = [&](int t) {
+    const char* vb = smem + (t % VSLOTS) * VT_BYTES;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= S) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[sb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // c turns a raw score of this tile into a base-2 logit (softmax scale,
-    // log2 e and both block scales).
-    const float kscale_t = ksc[kt];
-    float c[QB], tmax[QB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      c[qb] = cq[qb] * kscale_t;
-      float mx = sacc[0][qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][qb][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][qb][r]);
-      tmax[qb] = pair_max(mx) * c[qb];
-      grow = grow || (tmax[qb] > m[qb] + RESCALE_SLACK);
-    }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; rare after the first tile
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = tmax[qb] > m[qb] + RESCALE_SLACK ? tmax[qb] : m[qb];
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_new);  // 1 where m stays, 0 from -inf
-        m[qb] = m_new;
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-      }
-    }
-
-    bf16x8 pf[QB][2][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float rs = l[qb];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          // Packed into separate scalars first: a v_dot2 whose source is an
-          // element of a 128-bit vector is miscompiled by this toolchain (it
-          // reads element 0 every time).
-          unsigned pk[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][8 * hh + 2 * i], c[qb], -m[qb]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sb][qb][8 * hh + 2 * i + 1], c[qb], -m[qb]));
-            pk[i] = pack_bf16x2(p0, p1);
-            // row sum of the bf16 probabilities, the same values the PV product uses
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), BF16_ONES, rs, false);
-          }
-          const u32x4 w = {pk[0], pk[1], pk[2], pk[3]};
-          pf[qb][sb][hh] = __builtin_bit_cast(bf16x8, w);
-        }
-      l[qb] = rs;
-    }
-
-    // O^T += V^T P^T.
+      for (int db = 0; db < 4; ++db) fr[4 * hh + db] = v_frag(vb, 0, hh, db);
+  };
+  // O^T += V^T P^T for tile t (after pv_prefetch): 2 sub-blocks x 2 key
+  // halves x 4 value-dim blocks.
+  auto pv = [&](int t) {
+    const char* vb = smem + (t % VSLOTS) * VT_BYTES;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(sv + ((32 * db + l32) * VSTR + 32 * sb + 16 * hh + 8 * g) * 2);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][sb][hh], o[qb][db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[4 * hh + db], pf[sb][hh], o[db], 0, 0, 0);
+          if (sb == 0) fr[4 * hh + db] = v_frag(vb, 1, hh, db);
         }
   };
-
-  // All tiles but the last are full; the last one is masked.
-  for (int kt = 0; kt + 1 < n_kt; ++kt) {
-    const u32x4* kn = kg + int64_t(kt + 1) * TILE_CHUNKS;
-    const u32x4* vn = vg + int64_t(kt + 1) * TILE_CHUNKS;
+  // Online softmax of tile t (its scores in sc): mask the segment tail on the
+  // last tile, find the tile max, move the running max if needed, then form
+  // the bf16 probabilities and add their row sums to l.
+  //
+  // The running max m only moves when a tile's max exceeds it by more than
+  // RESCALE_SLACK; until then probabilities are exp2(t - m) <= 2^RESCALE_SLACK,
+  // which bf16 and fp32 hold without loss, and O and l need no rescaling.
+  // Exact either way: the final normalisation divides by an l built with the
+  // same m.  Every PV product issued so far used the old m, so rescaling O
+  // here keeps it consistent.
+  auto softmax = [&](int t) {
+    if (t == n_kt - 1 && (S % BK) != 0) {
+      const int kbase = t * BK;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      kreg[i] = kn[tid + i * NT];
-      vreg[i] = vn[tid + i * NT];
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3) >= S) sc[sb][r] = -INFINITY;
     }
-    tile_step(kt, std::false_type{});
-    store_stage((kt + 1) & 1);
-    __syncthreads();
-  }
-  tile_step(n_kt - 1, std::true_type{});
-
-  // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
+    // c turns a raw score of this tile into a base-2 logit (softmax scale,
+    // log2 e and both block scales).
+    const float c = cq * ksc[t];
+    float mx = sc[0][0];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = pair_sum(l[qb]);
-    const float inv = 1.0f / lt;
-    if (qrow[qb] < S) {
-      const int64_t tok = int64_t(seg_a) + qrow[qb];
-      u32x2* orow = out + (tok * n_heads + h) * (D / 4);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+    const float tmax = pair_max(mx) * c;
+    const bool grow = tmax > m + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; rare after the first tile
+      const float m_new = grow ? tmax : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 1 where m stays, 0 from -inf
+      m = m_new;
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          u32x2 w;
-          w[0] = pack_bf16x2(o[qb][db][4 * k4] * inv, o[qb][db][4 * k4 + 1] * inv);
-          w[1] = pack_bf16x2(o[qb][db][4 * k4 + 2] * inv, o[qb][db][4 * k4 + 3] * inv);
-          orow[db * 8 + 2 * k4 + g] = w;
-        }
-      if (g == 0) lse[int64_t(h) * n_tokens + tok] = (m[qb] + log2f(lt)) * 0.69314718055994531f;
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
+    float rs = 0.0f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[sb][8 * hh + 2 * i], c, -m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[sb][8 * hh + 2 * i + 1], c, -m));
+          w[i] = pack_bf16x2(p0, p1);
+          rs += p0 + p1;
+        }
+        pf[sb][hh] = __builtin_bit_cast(bf16x8, w);
+      }
+    l += rs;
+  };
+
+  __syncthreads();  // tile 0 has landed
+  const bool group_b = wave >= NW / 2;
+  if (!group_b) {
+    for (int t = 0; t < n_kt; ++t) {
+      if (t + 1 < n_kt) load_tiles(t + 1);
+      qk(t);
+      pv_prefetch(t);
+      softmax(t);
+      pv(t);
+      __syncthreads();  // tile t+1 has landed; reads of the slots refilled next are done
+    }
+  } else {
+    for (int t = 0; t < n_kt; ++t) {
+      if (t + 1 < n_kt) load_tiles(t + 1);
+      if (t > 0) {
+        pv_prefetch(t - 1);
+        softmax(t - 1);
+        pv(t - 1);
+      }
+      qk(t);
+      __syncthreads();
+    }
+    pv_prefetch(n_kt - 1);
+    softmax(n_kt - 1);
+    pv(n_kt - 1);
+  }
+
+  // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
+  const float lt = pair_sum(l);
+  const float inv = 1.0f / lt;
+  if (qrow < S) {
+    const int64_t tok = int64_t(seg_a) + qrow;
+    u32x2* orow = out + (tok * n_heads + h) * (D / 4);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[db][4 * k4] * inv, o[db][4 * k4 + 1] * inv);
+        w[1] = pack_bf16x2(o[db][4 * k4 + 2] * inv, o[db][4 * k4 + 3] * inv);
+        orow[db * 8 + 2 * k4 + g] = w;
+      }
+    if (g == 0) lse[int64_t(h) * n_tokens + tok] = (m + log2f(lt)) * 0.69314718055994531f;
   }
 }
-
-constexpr int ATTN_NW = 4;
-constexpr int ATTN_QB = 2;
-constexpr int ATTN_BQ = 32 * ATTN_NW * ATTN_QB;
-constexpr size_t ATTN_SMEM = 2 * STAGE_BYTES;
 
 }  // namespace
 
@@ -592,13 +617,13 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
   if (tiles == 0) return 0;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<ATTN_NW, ATTN_QB>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(ATTN_SMEM));
     if (e != hipSuccess) return int(e);
     attr_set = true;
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_fwd_kernel<ATTN_NW, ATTN_QB>), dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),
                      dim3(ATTN_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
                      pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
                      static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), k_scale, rows_per_head);

@@ -35,7 +35,7 @@ inline int64_t packed_rows(int64_t n_tokens, int32_t n_seqs) {
 
 // Workspace layout, in this order:
 //   keys    fp16 [H][rows][128]     rotated, each 64-key tile block-scaled
-//   values  bf16 [H][rows/64][128][64]  transposed tiles
+//   values  bf16 [H][rows/32][128][32]  transposed 32-key tiles
 //   scales  fp32 [H][rows/64]       per-tile factor that undoes the key scaling
 struct WorkspaceLayout {
   size_t keys_offset, values_offset, scales_offset, total;

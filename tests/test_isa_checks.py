@@ -3,12 +3,13 @@
 hipcc cross-compiles here, so properties of the generated code can be checked
 without a GPU:
 
-* The row sums use v_dot2c_f32_bf16 over packed bf16 probabilities.  This
-  toolchain miscompiles a dot2 whose source is an element of a 128-bit vector:
-  it reads element 0 for every call, so one pair is counted four times.  The
-  kernel avoids that form; this test fails if such a chain (the same
-  accumulator fed the same source register twice in a row) reappears.
-* No scratch (register spills) and no packed-fp32 instructions.
+* The score contraction runs on v_mfma_f32_32x32x16_f16 and the value
+  contraction on v_mfma_f32_32x32x16_bf16.
+* No vector-register spills, no scratch memory and no packed-fp32
+  instructions.  (Scalar spills go to vector-register lanes, not memory.)
+* If a v_dot2 chain appears, no accumulator is fed the same source register
+  twice in a row: this toolchain miscompiles a dot2 whose source is an element
+  of a 128-bit vector (it reads element 0 every time).
 """
 
 import os
@@ -33,14 +34,20 @@ def isa(tmp_path_factory):
     return out.read_text()
 
 
+def test_mfma_instructions(isa):
+    assert "v_mfma_f32_32x32x16_f16" in isa
+    assert "v_mfma_f32_32x32x16_bf16" in isa
+
+
 def test_dot2_chains_read_distinct_sources(isa):
     ops = re.findall(r"v_dot2c_f32_bf16_e32\s+(v\d+),\s*([^,\s]+),\s*(v\d+)", isa)
-    assert ops, "expected dot2 row sums in the attention kernel"
     for (acc0, _, src0), (acc1, _, src1) in zip(ops, ops[1:]):
         assert not (acc0 == acc1 and src0 == src1), f"dot2 chain on {acc0} reads {src0} twice in a row"
 
 
 def test_no_spills_and_no_packed_fp32(isa):
-    for m in re.finditer(r"\.(?:vgpr|sgpr)_spill_count:\s+(\d+)", isa):
-        assert int(m.group(1)) == 0
+    counts = re.findall(r"\.vgpr_spill_count:\s+(\d+)", isa)
+    assert counts and all(int(c) == 0 for c in counts)
+    scratch = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", isa)
+    assert scratch and all(int(c) == 0 for c in scratch)
     assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", isa)
