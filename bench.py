@@ -27,6 +27,37 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+# HBM bytes of one attn_fwd_kernel launch on the 1344x768 workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
+# plain 1 GiB device copy (FETCH_SIZE reports half of the bytes read, WRITE_SIZE all bytes written).
+# The figures hold only for the kernel source they were taken on; any other source reports null.
+HBM_COUNTERS = {
+    "workload": "1344x768",
+    "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
+    "source_sha256": "88edc735336852303fb2b1a633307e24d0e87027d77f7aa1f01b6b6dcb452d1a",
+    "fetch_kib": 3747430, "fetch_scale": 2.0,
+    "write_kib": 165119, "write_scale": 1.0,
+}
+
+
+def counted_traffic(workload):
+    """Calibrated HBM bytes per attention launch, or None when the counters do not apply."""
+    import hashlib
+
+    c = HBM_COUNTERS
+    if workload != c["workload"]:
+        return None
+    try:
+        with open(os.path.join(ROOT, c["source"]), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if digest != c["source_sha256"]:
+        return None
+    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+
+
 METRIC = "joint A/V attention TFLOP/s @ ~130k tokens; % of bf16 MFMA peak"
 
 
@@ -97,7 +128,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path runs on one GPU's head share and this build has no "
-              "multi-GPU mode (see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+              "multi-GPU mode (across GPUs it would shard by heads after an all-to-all). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -187,7 +218,7 @@ def main():
         "config": describe(name, cfg, N, len(lens)),
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counted_traffic(name),
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
     }

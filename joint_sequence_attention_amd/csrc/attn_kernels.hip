@@ -18,7 +18,7 @@
 //                       softmax between two bf16 MFMA contractions.
 //
 // MFMA orientation.  The score tile is computed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims (from LDS), B = 16 dims x
+// v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims (from LDS), B = 16 dims x
 // 32 queries (held in registers for the whole kernel).  In the 32x32
 // accumulator, lane L owns query column L % 32 and the 16 key rows
 // 8*(r/4) + 4*(L/32) + r%4, r = 0..15; the other 16 keys of that query sit in
@@ -41,6 +41,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -615,12 +616,17 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
                      const void* k_ws, const void* v_ws, const float* k_scale, int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + ATTN_BQ - 1) / ATTN_BQ);
   if (tiles == 0) return 0;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(ATTN_SMEM));
+  // The dynamic LDS limit is raised once per device.
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  static std::atomic<uint64_t> attr_set{0};
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit == 0 || (attr_set.load(std::memory_order_acquire) & bit) == 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(ATTN_SMEM));
     if (e != hipSuccess) return int(e);
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attn_fwd_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),

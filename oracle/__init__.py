@@ -28,7 +28,7 @@ What it computes (sources are the pages the method is described on):
 Every function is pinned by tests under ``tests/`` against closed forms,
 invariants, brute force and library routines (see ``tests/test_oracle_*.py``).
 The pages fix no numeric attention output, so agreement with the pages
-themselves rests on those pins and on the readings listed in the design doc.
+themselves rests on those pins and on the readings stated in each module.
 """
 
 from .layout import layout, round_half_even

@@ -4,8 +4,7 @@ Test infrastructure only; see the package docstring.
 
 The DiT's position encoding is rotary ("Day 0 Support for MiniMax-H3 on AMD
 Instinct GPUs", DiT property table).  The pages do not spell out the
-multi-axis form; the reading used here (listed with the other readings in
-DESIGN.md):
+multi-axis form; the reading used here:
 
 * the 128-wide head is split into consecutive axis chunks, t then h then w,
   of widths (32, 48, 48);
