@@ -35,9 +35,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
-    "source_sha256": "88edc735336852303fb2b1a633307e24d0e87027d77f7aa1f01b6b6dcb452d1a",
-    "fetch_kib": 3747430, "fetch_scale": 2.0,
-    "write_kib": 165119, "write_scale": 1.0,
+    "source_sha256": "1c2da264e902aea9d4b3783313f8893d9e928350660ed93bd19913cf4212cc13",
+    "fetch_kib": 3669052, "fetch_scale": 2.0,
+    "write_kib": 165111, "write_scale": 1.0,
 }
 
 
