@@ -12,10 +12,11 @@
 //   kv_prologue_kernel  rotates K once per call and packs it, with V
 //                       transposed, into 64-key tiles that start on a 64-key
 //                       boundary for every segment.  HBM-bound.
-//   attn_fwd_kernel     one workgroup per (query tile, segment, head).  It
-//                       rotates its queries while loading them, then streams
-//                       the segment's key tiles through LDS and runs an online
-//                       softmax between two bf16 MFMA contractions.
+//   attn_fwd_kernel     one workgroup per (256-query tile, segment, head).
+//                       It rotates its queries while loading them, then
+//                       streams the segment's 32-key tiles through LDS and
+//                       runs an online softmax between two MFMA contractions,
+//                       software-pipelined inside each wave.
 //
 // MFMA orientation.  The score tile is computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims (from LDS), B = 16 dims x
@@ -25,7 +26,7 @@
 // lane L ^ 32.  So a row maximum or row sum is an in-lane reduction plus one
 // v_permlane32_swap.  The probabilities then serve directly as the B operand
 // of O^T += V^T P^T (keys are the contraction index), with no data movement:
-// registers 8*hh .. 8*hh+7 of a sub-block hold 8 keys of one 16-key group.
+// registers 8*hh .. 8*hh+7 of a 32-key tile hold 8 keys of one 16-key group.
 // The prologue stores V^T with its keys permuted inside each 16-key group so
 // that the matching A operand (8 keys of one value dim) is one contiguous
 // 16-byte LDS read.
@@ -288,105 +289,130 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Attention forward.  Eight waves per workgroup, one 32-row query block per
-// wave; BQ = 256 query rows per workgroup.
-// grid = (query tiles of the longest segment, segments, heads).
+// Attention forward, software-pipelined inside each wave.
 //
-// Ping-pong schedule.  Waves 0-3 (group A) and waves 4-7 (group B) land one
-// of each on every SIMD and work through the same 64-key tiles half a phase
-// apart.  Between two barriers, for tile t:
-//   group A:  S(t) = K(t) Q^T  |  softmax(t)    |  O += V(t) P(t)
-//   group B:  softmax(t-1)     |  O += V(t-1) P(t-1)  |  S(t) = K(t) Q^T
-// so while one wave of a SIMD runs its softmax (VALU) the other issues MFMAs.
-// Each wave's own code stays in plain order; the overlap comes from the two
-// waves.  Group B finishes its last tile after the loop.
+// Eight waves per workgroup, two per SIMD, one 32-row query block per wave:
+// BQ = 256 query rows per workgroup.  Keys arrive in 32-key tiles.  Iteration
+// t of the main loop issues, in one branch-free block of 16 slots,
+//     S(t+1) = K(t+1) Q^T     8 MFMAs (f16), even slots
+//     O     += V(t-1) P(t-1)  8 MFMAs (bf16), odd slots
+// and, between them, the exponentials of tile t, so that the matrix core and
+// the vector ALU of the SIMD work at the same time (and the second wave of
+// the SIMD fills what one wave leaves idle).
 //
-// LDS: a ring of two key tiles (16 KiB each) and three value tiles (group B
-// reads value tile t-1 while tile t+1 is being filled), filled by direct
-// global->LDS loads one tile ahead.  Rows are not padded; 16-byte chunks are
-// XOR-swizzled so that every fragment read (16 lanes on 16 different rows,
-// same logical chunk) touches each bank once:
-//   key tile         64 rows x 16 chunks: chunk c of row r at r*256 + 16*(c ^ (r & 15))
-//   value sub-tile  128 rows x  4 chunks: chunk c of row d at d*64 + 16*(c ^ ((d >> 2) & 3))
-// (a 64-key value tile is two 32-key sub-tiles, as in the workspace).
+// Online softmax in base 2 with a lazily moved running max m: the
+// probabilities of tile t are formed as exp2(s*c - m) with the current m.
+// A lane whose row sum for the tile exceeds 2^LAZY_LOG2 (or is not finite,
+// as on the first tile where m = -inf) sends the wave down a rare path that
+// takes the exact tile max, moves m, rescales l and O and recomputes the
+// tile's probabilities.  Until then every probability is at most
+// 2^LAZY_LOG2, well inside bf16 and fp32 range, and nothing is rescaled.
+// The result is exact softmax either way: O and l always share one m.
+//
+// LDS: rings of four key slots and four value slots of 8 KiB.  Iteration t
+// reads K(t+1) and V(t-1) and issues direct global->LDS loads of K(t+4) and
+// V(t+2), three iterations ahead; the barrier that ends an iteration waits
+// only for the loads issued before the previous two iterations.  The loop is
+// unrolled by four so that every slot offset is an immediate.
 // ---------------------------------------------------------------------------
-constexpr int KT_BYTES = BK * D * 2;    // 16 KiB key tile
-constexpr int VT_BYTES = BK * D * 2;    // 16 KiB value tile (two sub-tiles of 8 KiB)
-constexpr int KSLOTS = 2, VSLOTS = 3;
-constexpr float RESCALE_SLACK = 8.0f;  // base-2 logit units the running max may lag behind
-
 __device__ __forceinline__ int k_lds_offset(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ ((d >> 2) & 3)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int ATTN_NW = 8;
-constexpr int ATTN_BQ = 32 * ATTN_NW;
-constexpr size_t ATTN_SMEM = KSLOTS * KT_BYTES + VSLOTS * VT_BYTES;
+constexpr int PK = 32;                              // keys per tile
+constexpr int P_NW = 8;                             // waves per workgroup
+constexpr int ATTN_BQ = 32 * P_NW;                  // 256 query rows per workgroup
+constexpr int P_TILE_BYTES = PK * D * 2;            // 8 KiB
+constexpr int P_TILE_CHUNKS = PK * CHUNKS_PER_ROW;  // 512 16-byte chunks
+constexpr int P_NS = 4;                             // slots per ring
+constexpr int P_VBASE = P_NS * P_TILE_BYTES;        // value ring after the key ring
+constexpr size_t ATTN_SMEM = 2 * P_NS * P_TILE_BYTES;  // 64 KiB
+constexpr float LAZY_LOG2 = 16.0f;                  // log2 of the largest row sum left unrescaled
 
-__global__ __launch_bounds__(ATTN_NW * 64, 1) void attn_fwd_kernel(
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// Wait until at most N vector-memory operations of this wave are in flight,
+// then meet the other waves.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Pins a value to the point where this is called: the compiler may neither
+// compute it later nor fold it into later code.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
+
+__global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const u32x4* __restrict__ k_ws, const u32x4* __restrict__ v_ws, const float* __restrict__ k_scale,
     int64_t rows_per_head) {
-  constexpr int NW = ATTN_NW;
-  constexpr int NT = NW * 64;
-  constexpr int BQ = ATTN_BQ;
-  constexpr int LOADS = TILE_CHUNKS / NT;  // direct-load instructions per wave per tile and tensor
-  static_assert(TILE_CHUNKS % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(P_TILE_CHUNKS == P_NW * 64, "one direct load per wave, tile and tensor");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // key slots, then value slots
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
 
   const int qt = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const int32_t seg_a = cu[s];
   const int32_t S = cu[s + 1] - seg_a;
-  if (qt * BQ >= S) return;  // whole block leaves together
+  if (qt * ATTN_BQ >= S) return;  // whole block leaves together
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   stage_rope_table(tab, s_omega, s_axis);
 
-  const int n_kt = (S + BK - 1) / BK;
+  const int n_kt = (S + PK - 1) / PK;
+  const int last_t = n_kt - 1;
+  const bool ragged = (S % PK) != 0;
   const int64_t prow = packed_start(seg_a, s);
-  const u32x4* kg = k_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
-  const u32x4* vg = v_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW;
-  const float* ksc = k_scale + int64_t(h) * (rows_per_head / BK) + prow / BK;
+  const char* kg = reinterpret_cast<const char*>(k_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW);
+  const char* vg = reinterpret_cast<const char*>(v_ws + (int64_t(h) * rows_per_head + prow) * CHUNKS_PER_ROW);
+  const float* ksc = k_scale + int64_t(h) * (rows_per_head / 64) + prow / 64;  // one factor per 64 keys
 
-  // Lane L of load instruction i fills LDS chunk p = (i*NW + wave)*64 + L of
-  // the tile, so it fetches the logical chunk the swizzle puts there.
-  auto load_tiles = [&](int t) {
-    const u32x4* ksrc = kg + int64_t(t) * TILE_CHUNKS;
-    const u32x4* vsrc = vg + int64_t(t) * TILE_CHUNKS;
-    char* kdst = smem + (t % KSLOTS) * KT_BYTES;
-    char* vdst = smem + KSLOTS * KT_BYTES + (t % VSLOTS) * VT_BYTES;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int p = (i * NW + wave) * 64 + lane;
-      const int r = p >> 4, c = (p & 15) ^ (r & 15);
-      __builtin_amdgcn_global_load_lds(ksrc + r * CHUNKS_PER_ROW + c, (lds_void*)(kdst + (i * NW + wave) * 1024), 16,
-                                       0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int p = (i * NW + wave) * 64 + lane;
-      const int sub = p >> 9, qq = p & 511;
-      const int d = qq >> 2, c = (qq & 3) ^ ((d >> 2) & 3);
-      __builtin_amdgcn_global_load_lds(vsrc + sub * 512 + d * 4 + c, (lds_void*)(vdst + (i * NW + wave) * 1024), 16,
-                                       0, 0);
-    }
+  // Direct loads: lane L of wave w fills LDS chunk p = 64*w + L of a slot, so
+  // it fetches the logical chunk that the swizzle puts there.  The per-lane
+  // source offsets are the same for every tile.
+  unsigned ksrc_off, vsrc_off;
+  {
+    const int p = wave * 64 + lane;
+    const int r = p >> 4, c = (p & 15) ^ (r & 15);
+    ksrc_off = unsigned(r * CHUNKS_PER_ROW + c) * 16u;
+    const int d = p >> 2, cv = (p & 3) ^ ((d >> 2) & 3);
+    vsrc_off = unsigned(d * 4 + cv) * 16u;
+  }
+  auto load_k = [&](int t, auto SLOT) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    __builtin_amdgcn_global_load_lds(kg + int64_t(t) * P_TILE_BYTES + ksrc_off,
+                                     (lds_void*)(smem + slot * P_TILE_BYTES + wave * 1024), 16, 0, 0);
+  };
+  auto load_v = [&](int t, auto SLOT) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    __builtin_amdgcn_global_load_lds(vg + int64_t(t) * P_TILE_BYTES + vsrc_off,
+                                     (lds_void*)(smem + P_VBASE + slot * P_TILE_BYTES + wave * 1024), 16, 0, 0);
   };
 
-  load_tiles(0);  // first tile loads while the queries are rotated
-  __syncthreads();  // rope table staged
+  load_k(0, ic<0>());
+  load_k(min(1, last_t), ic<1>());
+  __syncthreads();  // rope table staged; K(0) and K(1) have landed
+  // The loads iterations -2 and -1 would have issued, in the same order.
+  load_k(min(2, last_t), ic<2>());
+  load_v(0, ic<0>());
+  load_k(min(3, last_t), ic<3>());
+  load_v(min(1, last_t), ic<1>());
 
-  // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 of its block
-  // and dims 16*ks + 8*g .. +7, rotated in fp32, scaled by the row's
-  // power-of-two factor and rounded to fp16; cq folds the undoing factor into
-  // the base-2 logit coefficient.
+  // Queries: B operand of S^T = K Q^T.  The lane holds query row l32 and dims
+  // 16*ks + 8*g .. +7, rotated in fp32, scaled by the row's power-of-two
+  // factor and rounded to fp16; cq folds the undoing factor into the base-2
+  // logit coefficient.
+  const int qrow = qt * ATTN_BQ + wave * 32 + l32;
   f16x8 qf[8];
   float cq;
-  const int qrow = qt * BQ + wave * 32 + l32;
   {
     float f[8][8];
     if (qrow < S) {
@@ -415,13 +441,13 @@ __global__ __launch_bounds__(ATTN_NW * 64, 1) void attn_fwd_kernel(
     for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(f16x8, pack8_f16(f[ks], down));
   }
 
-  // Per-lane fragment offsets within a slot (the sub-block / value-dim
-  // block / sub-tile parts are immediate offsets on top).
+  // Per-lane fragment offsets inside a slot; slot and sub-block parts are
+  // immediates.
   int koff[8], voff[2];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) koff[ks] = k_lds_offset(l32, 2 * ks + g);
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) voff[hh] = KSLOTS * KT_BYTES + v_lds_offset(l32, 2 * hh + g);
+  for (int hh = 0; hh < 2; ++hh) voff[hh] = v_lds_offset(l32, 2 * hh + g);
 
   f32x16 o[4];
 #pragma unroll
@@ -429,140 +455,211 @@ __global__ __launch_bounds__(ATTN_NW * 64, 1) void attn_fwd_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = -INFINITY, l = 0.0f;
-  f32x16 sc[2];       // S^T of one 64-key tile (two 32-key sub-blocks)
-  bf16x8 pf[2][2];    // its probabilities, [sub-block][key half]
+  float ct = cq * ksc[0];   // base-2 logit coefficient of the tile whose exponentials come next
+  f32x16 sc[2];             // S^T of one tile, double-buffered by tile parity
+  bf16x8 pf[2][2];          // its probabilities, [buffer][key half]
 
-  // Fragment prefetch: LDS reads take longer than an MFMA, so each chain's
-  // operands are read eight ahead and a register is refilled as soon as its
-  // MFMA has been issued.
-  bf16x8 fr[8];
-  auto k_frag = [&](const char* kb, int sb, int ks) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + sb * 32 * 256 + koff[ks]));
+  auto kfrag = [&](auto SLOT, int ks) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    return *reinterpret_cast<const u32x4*>(smem + slot * P_TILE_BYTES + koff[ks]);
   };
-  auto v_frag = [&](const char* vb, int sb, int hh, int db) {
-    return *reinterpret_cast<const bf16x8*>(vb + sb * (VT_BYTES / 2) + db * 32 * 64 + voff[hh]);
+  auto vfrag = [&](auto SLOT, int f) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    return *reinterpret_cast<const bf16x8*>(smem + P_VBASE + slot * P_TILE_BYTES + (f & 3) * 32 * 64 + voff[f >> 2]);
   };
-  // S^T for tile t: 2 sub-blocks x 8 MFMAs over the head dim.
-  auto qk = [&](int t) {
-    const char* kb = smem + (t % KSLOTS) * KT_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) fr[ks] = k_frag(kb, 0, ks);
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[sb][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fr[ks]), qf[ks], sc[sb], 0, 0, 0);
-        if (sb == 0) fr[ks] = k_frag(kb, 1, ks);
-      }
-    }
+  auto mfma_qk = [&](f32x16 acc, u32x4 kf, int ks) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf), qf[ks], acc, 0, 0, 0);
   };
-  // First eight value fragments of tile t (sub-block 0), read ahead of the
-  // softmax so they arrive while it runs.
-  auto pv_prefetch = [&](int t) {
-    const char* vb = smem + (t % VSLOTS) * VT_BYTES;
+
+  // S^T(t) into buffer B, alone (pipeline fill).
+  auto qk_alone = [&](auto B, auto SLOT) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    f32x16 acc;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) fr[4 * hh + db] = v_frag(vb, 0, hh, db);
+    for (int ks = 0; ks < 8; ++ks) acc = mfma_qk(acc, kfrag(SLOT, ks), ks);
+    sc[b] = acc;
   };
-  // O^T += V^T P^T for tile t (after pv_prefetch): 2 sub-blocks x 2 key
-  // halves x 4 value-dim blocks.
-  auto pv = [&](int t) {
-    const char* vb = smem + (t % VSLOTS) * VT_BYTES;
+  // O^T += V^T(t) P^T(t) from buffer B, alone (pipeline drain).
+  auto pv_alone = [&](auto B, auto SLOT) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[4 * hh + db], pf[sb][hh], o[db], 0, 0, 0);
-          if (sb == 0) fr[4 * hh + db] = v_frag(vb, 1, hh, db);
-        }
+    for (int f = 0; f < 8; ++f)
+      o[f & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(SLOT, f), pf[b][f >> 2], o[f & 3], 0, 0, 0);
   };
-  // Online softmax of tile t (its scores in sc): mask the segment tail on the
-  // last tile, find the tile max, move the running max if needed, then form
-  // the bf16 probabilities and add their row sums to l.
-  //
-  // The running max m only moves when a tile's max exceeds it by more than
-  // RESCALE_SLACK; until then probabilities are exp2(t - m) <= 2^RESCALE_SLACK,
-  // which bf16 and fp32 hold without loss, and O and l need no rescaling.
-  // Exact either way: the final normalisation divides by an l built with the
-  // same m.  Every PV product issued so far used the old m, so rescaling O
-  // here keeps it consistent.
-  auto softmax = [&](int t) {
-    if (t == n_kt - 1 && (S % BK) != 0) {
-      const int kbase = t * BK;
+  // Keys of tile t at or past the segment end get score -inf.
+  auto mask_tail = [&](auto B, int t) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    const int kbase = t * PK;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int r = 0; r < 16; ++r)
+      if (kbase + 8 * (r >> 2) + 4 * g + (r & 3) >= S) sc[b][r] = -INFINITY;
+  };
+  // Probabilities of the scores in buffer B at the current m: unit u covers
+  // registers 2u and 2u+1 (key half u >> 2).
+  auto exp_unit = [&](auto B, int u, u32x4 (&pw)[2], float& rs) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u], ct, -m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u + 1], ct, -m));
+    unsigned w = pack_bf16x2(p0, p1);
+    float r = u == 0 ? p0 + p1 : rs + (p0 + p1);
+    pin(w);
+    pin(r);
+    pw[u >> 2][u & 3] = w;
+    rs = r;
+  };
+  // After the exponentials of tile t (scores in buffer B, products of tile
+  // t-1 issued): the rare path that moves m, then the row sums and the
+  // probabilities for the next products.
+  auto settle = [&](auto B, u32x4 (&pw)[2], float rs) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    const bool over = !(rs <= exp2f(LAZY_LOG2));  // also true for inf and NaN
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      float mx = sc[b][0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + 32 * sb + 8 * (r >> 2) + 4 * g + (r & 3) >= S) sc[sb][r] = -INFINITY;
-    }
-    // c turns a raw score of this tile into a base-2 logit (softmax scale,
-    // log2 e and both block scales).
-    const float c = cq * ksc[t];
-    float mx = sc[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    const float tmax = pair_max(mx) * c;
-    const bool grow = tmax > m + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; rare after the first tile
-      const float m_new = grow ? tmax : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 1 where m stays, 0 from -inf
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
+      const float tmax = pair_max(mx) * ct;
+      const float m_new = fmaxf(m, tmax);
+      const float a = __builtin_amdgcn_exp2f(m - m_new);  // 0 from m = -inf
       m = m_new;
-      l *= alpha;
+      l *= a;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    float rs = 0.0f;
+        for (int r = 0; r < 16; ++r) o[db][r] *= a;
+      rs = 0.0f;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[sb][8 * hh + 2 * i], c, -m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[sb][8 * hh + 2 * i + 1], c, -m));
-          w[i] = pack_bf16x2(p0, p1);
-          rs += p0 + p1;
-        }
-        pf[sb][hh] = __builtin_bit_cast(bf16x8, w);
+      for (int u = 0; u < 8; ++u) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u], ct, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u + 1], ct, -m));
+        pw[u >> 2][u & 3] = pack_bf16x2(p0, p1);
+        rs += p0 + p1;
       }
+    }
     l += rs;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) pf[b][hh] = __builtin_bit_cast(bf16x8, pw[hh]);
   };
 
-  __syncthreads();  // tile 0 has landed
-  const bool group_b = wave >= NW / 2;
-  if (!group_b) {
-    for (int t = 0; t < n_kt; ++t) {
-      if (t + 1 < n_kt) load_tiles(t + 1);
-      qk(t);
-      pv_prefetch(t);
-      softmax(t);
-      pv(t);
-      __syncthreads();  // tile t+1 has landed; reads of the slots refilled next are done
+  // The main block of iteration t for T4 = t mod 4 (S(t) in sc[t & 1]):
+  // 16 issue slots alternating S(t+1) MFMAs (when QK) and O += V(t-1) P(t-1)
+  // MFMAs (when PV), one exponential unit on every even slot, fragment reads
+  // two slots ahead.  A scheduling fence after every slot keeps this order.
+  auto region = [&](auto T4, auto QK, auto PV, u32x4 (&pw)[2], float& rs) __attribute__((always_inline)) {
+    constexpr int t4 = decltype(T4)::value;
+    constexpr int b = t4 & 1;
+    constexpr bool do_qk = decltype(QK)::value != 0;
+    constexpr bool do_pv = decltype(PV)::value != 0;
+    constexpr ic<(t4 + 1) & 3> kslot{};  // K(t+1)
+    constexpr ic<(t4 + 3) & 3> vslot{};  // V(t-1)
+    u32x4 kf[8];
+    bf16x8 vf[8];
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    if (do_qk) {
+      kf[0] = kfrag(kslot, 0);
+      kf[1] = kfrag(kslot, 1);
     }
-  } else {
-    for (int t = 0; t < n_kt; ++t) {
-      if (t + 1 < n_kt) load_tiles(t + 1);
-      if (t > 0) {
-        pv_prefetch(t - 1);
-        softmax(t - 1);
-        pv(t - 1);
+    if (do_pv) {
+      vf[0] = vfrag(vslot, 0);
+      vf[1] = vfrag(vslot, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = j >> 1;
+      if ((j & 1) == 0) {
+        if (do_qk) {
+          acc = mfma_qk(acc, kf[i], i);
+          if (i + 2 < 8) kf[i + 2] = kfrag(kslot, i + 2);
+        }
+        exp_unit(ic<b>(), i, pw, rs);
+      } else if (do_pv) {
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[1 - b][i >> 2], o[i & 3], 0, 0, 0);
+        if (i + 2 < 8) vf[i + 2] = vfrag(vslot, i + 2);
       }
-      qk(t);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    pv_prefetch(n_kt - 1);
-    softmax(n_kt - 1);
-    pv(n_kt - 1);
+    if (do_qk) sc[1 - b] = acc;
+  };
+
+  // Steady iteration t (1 <= t <= last_t - 1), T4 = t mod 4.  Loads K(t+4)
+  // into the slot of K(t) and V(t+2) into the slot of V(t-2), both read for
+  // the last time in iteration t-1.  Past the last tile the index is
+  // clamped: the duplicate goes to a slot that is not read again, and every
+  // iteration keeps issuing exactly two loads, which the ring barrier counts.
+  auto step = [&](auto T4, int t) __attribute__((always_inline)) {
+    constexpr int t4 = decltype(T4)::value;
+    load_k(min(t + 4, last_t), ic<t4>());
+    load_v(min(t + 2, last_t), ic<(t4 + 2) & 3>());
+    u32x4 pw[2];
+    float rs;
+    region(T4, ic<1>(), ic<1>(), pw, rs);
+    settle(ic<t4 & 1>(), pw, rs);
+    ct = cq * ksc[(t + 1) >> 1];
+    ring_barrier<4>();  // K(t+2) and V(t), issued in iteration t-2, have landed
+  };
+  // Last iteration t = last_t >= 1: exponentials of tile t and products of
+  // tile t-1, then the products of tile t.
+  auto last = [&](auto T4) __attribute__((always_inline)) {
+    constexpr int t4 = decltype(T4)::value;
+    if (ragged) mask_tail(ic<t4 & 1>(), last_t);
+    u32x4 pw[2];
+    float rs;
+    region(T4, ic<0>(), ic<1>(), pw, rs);
+    settle(ic<t4 & 1>(), pw, rs);
+    ring_barrier<0>();  // V(t) has landed
+    pv_alone(ic<t4 & 1>(), ic<t4>());
+  };
+
+  qk_alone(ic<0>(), ic<0>());
+  if (n_kt == 1) {
+    if (ragged) mask_tail(ic<0>(), 0);
+    u32x4 pw[2];
+    float rs;
+    region(ic<0>(), ic<0>(), ic<0>(), pw, rs);
+    settle(ic<0>(), pw, rs);
+    ring_barrier<0>();
+    pv_alone(ic<0>(), ic<0>());
+  } else {
+    ring_barrier<4>();  // every wave is done with K(0) before its slot is refilled
+    {
+      // t = 0: no products of an earlier tile yet.
+      load_k(min(4, last_t), ic<0>());
+      load_v(min(2, last_t), ic<2>());
+      u32x4 pw[2];
+      float rs;
+      region(ic<0>(), ic<1>(), ic<0>(), pw, rs);
+      settle(ic<0>(), pw, rs);
+      ct = cq * ksc[1 >> 1];
+      ring_barrier<4>();
+    }
+    int t = 1;
+    for (; t + 3 <= last_t - 1; t += 4) {
+      step(ic<1>(), t);
+      step(ic<2>(), t + 1);
+      step(ic<3>(), t + 2);
+      step(ic<0>(), t + 3);
+    }
+    if (t <= last_t - 1) {
+      step(ic<1>(), t);
+      ++t;
+      if (t <= last_t - 1) {
+        step(ic<2>(), t);
+        ++t;
+        if (t <= last_t - 1) {
+          step(ic<3>(), t);
+          ++t;
+        }
+      }
+    }
+    switch (last_t & 3) {
+      case 0: last(ic<0>()); break;
+      case 1: last(ic<1>()); break;
+      case 2: last(ic<2>()); break;
+      default: last(ic<3>()); break;
+    }
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
@@ -583,7 +680,6 @@ __global__ __launch_bounds__(ATTN_NW * 64, 1) void attn_fwd_kernel(
     if (g == 0) lse[int64_t(h) * n_tokens + tok] = (m + log2f(lt)) * 0.69314718055994531f;
   }
 }
-
 }  // namespace
 
 const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
@@ -630,7 +726,7 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(attn_fwd_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),
-                     dim3(ATTN_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
+                     dim3(P_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
                      pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
                      static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), k_scale, rows_per_head);
   return int(hipGetLastError());
