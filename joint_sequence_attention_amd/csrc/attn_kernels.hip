@@ -310,10 +310,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 // The result is exact softmax either way: O and l always share one m.
 //
 // LDS: rings of four key slots and four value slots of 8 KiB.  Iteration t
-// reads K(t+1) and V(t-1) and issues direct global->LDS loads of K(t+4) and
+// reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+4) and
 // V(t+2), three iterations ahead; the barrier that ends an iteration waits
 // only for the loads issued before the previous two iterations.  The loop is
-// unrolled by four so that every slot offset is an immediate.
+// unrolled by four so that every slot offset is an immediate.  (Buffer rather
+// than global loads: the compiler counts a global->LDS load as touching both
+// memory counters and would then wait for every LDS read in full.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int k_lds_offset(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ ((d >> 2) & 3)); }
@@ -386,15 +388,20 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     const int d = p >> 2, cv = (p & 3) ^ ((d >> 2) & 3);
     vsrc_off = unsigned(d * 4 + cv) * 16u;
   }
+  // Buffer resources over this head's segment of the key and value planes
+  // (tiles 0 .. n_kt-1); loads past the end read zeros.
+  const int seg_bytes = n_kt * P_TILE_BYTES;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, seg_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, seg_bytes, 0x00020000);
   auto load_k = [&](int t, auto SLOT) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOT)::value;
-    __builtin_amdgcn_global_load_lds(kg + int64_t(t) * P_TILE_BYTES + ksrc_off,
-                                     (lds_void*)(smem + slot * P_TILE_BYTES + wave * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + slot * P_TILE_BYTES + wave * 1024), 16, ksrc_off,
+                                             t * P_TILE_BYTES, 0, 0);
   };
   auto load_v = [&](int t, auto SLOT) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOT)::value;
-    __builtin_amdgcn_global_load_lds(vg + int64_t(t) * P_TILE_BYTES + vsrc_off,
-                                     (lds_void*)(smem + P_VBASE + slot * P_TILE_BYTES + wave * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + P_VBASE + slot * P_TILE_BYTES + wave * 1024), 16,
+                                             vsrc_off, t * P_TILE_BYTES, 0, 0);
   };
 
   load_k(0, ic<0>());
