@@ -294,8 +294,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 // Eight waves per workgroup, two per SIMD, one 32-row query block per wave:
 // BQ = 256 query rows per workgroup.  Keys arrive in 32-key tiles.  Iteration
 // t of the main loop issues, in one branch-free block of 16 slots,
-//     S(t+1) = K(t+1) Q^T     8 MFMAs (f16), even slots
-//     O     += V(t-1) P(t-1)  8 MFMAs (bf16), odd slots
+//     S(t+1) = K(t+1) Q^T     8 MFMAs (f16)
+//     O     += V(t-1) P(t-1)  8 MFMAs (bf16)
 // and, between them, the exponentials of tile t, so that the matrix core and
 // the vector ALU of the SIMD work at the same time (and the second wave of
 // the SIMD fills what one wave leaves idle).
@@ -310,12 +310,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 // The result is exact softmax either way: O and l always share one m.
 //
 // LDS: rings of four key slots and four value slots of 8 KiB.  Iteration t
-// reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+4) and
+// reads K(t+1) and V(t-1) and issues direct global->LDS loads of K(t+4) and
 // V(t+2), three iterations ahead; the barrier that ends an iteration waits
 // only for the loads issued before the previous two iterations.  The loop is
-// unrolled by four so that every slot offset is an immediate.  (Buffer rather
-// than global loads: the compiler counts a global->LDS load as touching both
-// memory counters and would then wait for every LDS read in full.)
+// unrolled by four so that every slot offset is an immediate.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int k_lds_offset(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ ((d >> 2) & 3)); }
@@ -503,12 +501,17 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     for (int r = 0; r < 16; ++r)
       if (kbase + 8 * (r >> 2) + 4 * g + (r & 3) >= S) sc[b][r] = -INFINITY;
   };
-  // Probabilities of the scores in buffer B at the current m: unit u covers
-  // registers 2u and 2u+1 (key half u >> 2).
-  auto exp_unit = [&](auto B, int u, u32x4 (&pw)[2], float& rs) __attribute__((always_inline)) {
+  // Probabilities of the scores in buffer B at the current m, in units u of
+  // two (registers 2u and 2u+1, key half u >> 2), each split in two halves:
+  // the exponentials, then the bf16 packing and the row-sum update.
+  auto exp_half_a = [&](auto B, int u, float& p0, float& p1) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u], ct, -m));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u + 1], ct, -m));
+    p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u], ct, -m));
+    p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][2 * u + 1], ct, -m));
+    pin(p0);
+    pin(p1);
+  };
+  auto exp_half_b = [&](int u, float p0, float p1, u32x4 (&pw)[2], float& rs) __attribute__((always_inline)) {
     unsigned w = pack_bf16x2(p0, p1);
     float r = u == 0 ? p0 + p1 : rs + (p0 + p1);
     pin(w);
@@ -550,9 +553,13 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
   };
 
   // The main block of iteration t for T4 = t mod 4 (S(t) in sc[t & 1]):
-  // 16 issue slots alternating S(t+1) MFMAs (when QK) and O += V(t-1) P(t-1)
-  // MFMAs (when PV), one exponential unit on every even slot, fragment reads
-  // two slots ahead.  A scheduling fence after every slot keeps this order.
+  // 16 issue slots.  Slots 0..7 issue the S(t+1) MFMAs (when QK) as one
+  // accumulation chain, slots 8..15 the O += V(t-1) P(t-1) MFMAs (when PV)
+  // with the four of each key half back to back, so that consecutive MFMAs
+  // share an operand or an accumulator (less switching, less energy on a
+  // power-limited chip).  The first half of an exponential unit follows every
+  // even slot and its second half every odd slot; fragment reads run two to
+  // four slots ahead.  A scheduling fence after every slot keeps this order.
   auto region = [&](auto T4, auto QK, auto PV, u32x4 (&pw)[2], float& rs) __attribute__((always_inline)) {
     constexpr int t4 = decltype(T4)::value;
     constexpr int b = t4 & 1;
@@ -562,30 +569,36 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     constexpr ic<(t4 + 3) & 3> vslot{};  // V(t-1)
     u32x4 kf[8];
     bf16x8 vf[8];
+    float ep0 = 0.0f, ep1 = 0.0f;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    // Value MFMA k (k = 0..7) uses key half k >> 2 and value-dim block k & 3.
     if (do_qk) {
       kf[0] = kfrag(kslot, 0);
       kf[1] = kfrag(kslot, 1);
     }
     if (do_pv) {
-      vf[0] = vfrag(vslot, 0);
-      vf[1] = vfrag(vslot, 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vf[k] = vfrag(vslot, k);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int i = j >> 1;
-      if ((j & 1) == 0) {
+      if (j < 8) {
         if (do_qk) {
-          acc = mfma_qk(acc, kf[i], i);
-          if (i + 2 < 8) kf[i + 2] = kfrag(kslot, i + 2);
+          acc = mfma_qk(acc, kf[j], j);
+          if (j + 2 < 8) kf[j + 2] = kfrag(kslot, j + 2);
         }
-        exp_unit(ic<b>(), i, pw, rs);
+        if (do_pv && j >= 4) vf[j] = vfrag(vslot, j);
       } else if (do_pv) {
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[1 - b][i >> 2], o[i & 3], 0, 0, 0);
-        if (i + 2 < 8) vf[i + 2] = vfrag(vslot, i + 2);
+        const int k = j - 8, hh = k >> 2, db = k & 3;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k], pf[1 - b][hh], o[db], 0, 0, 0);
       }
+      if ((j & 1) == 0)
+        exp_half_a(ic<b>(), i, ep0, ep1);
+      else
+        exp_half_b(i, ep0, ep1, pw, rs);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (do_qk) sc[1 - b] = acc;
