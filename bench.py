@@ -35,9 +35,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
-    "source_sha256": "1c2da264e902aea9d4b3783313f8893d9e928350660ed93bd19913cf4212cc13",
-    "fetch_kib": 3669052, "fetch_scale": 2.0,
-    "write_kib": 165111, "write_scale": 1.0,
+    "source_sha256": "7d3078f57dc85f252d8222f68aaa3eb9ca3f35a57b184fcf849b16fd00a78f7c",
+    "fetch_kib": 9252052, "fetch_scale": 2.0,
+    "write_kib": 165104, "write_scale": 1.0,
 }
 
 
