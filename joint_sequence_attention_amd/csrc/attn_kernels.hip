@@ -309,11 +309,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 // 2^LAZY_LOG2, well inside bf16 and fp32 range, and nothing is rescaled.
 // The result is exact softmax either way: O and l always share one m.
 //
-// LDS: rings of four key slots and four value slots of 8 KiB.  Iteration t
-// reads K(t+1) and V(t-1) and issues direct global->LDS loads of K(t+4) and
-// V(t+2), three iterations ahead; the barrier that ends an iteration waits
-// only for the loads issued before the previous two iterations.  The loop is
-// unrolled by four so that every slot offset is an immediate.
+// LDS: rings of eight key slots and eight value slots of 8 KiB.  Iteration t
+// reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+5) and
+// V(t+3), four iterations ahead.  Iterations pair up into epochs that end
+// with one barrier, which waits only for loads issued before the epoch.  The
+// loop is unrolled by eight so that every slot offset is an immediate.
+// (Buffer rather than global loads: the compiler counts a global->LDS load
+// as touching both memory counters and would then wait for every LDS read in
+// full while one is in flight.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int k_lds_offset(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ ((d >> 2) & 3)); }
@@ -325,9 +328,9 @@ constexpr int P_NW = 8;                             // waves per workgroup
 constexpr int ATTN_BQ = 32 * P_NW;                  // 256 query rows per workgroup
 constexpr int P_TILE_BYTES = PK * D * 2;            // 8 KiB
 constexpr int P_TILE_CHUNKS = PK * CHUNKS_PER_ROW;  // 512 16-byte chunks
-constexpr int P_NS = 4;                             // slots per ring
+constexpr int P_NS = 8;                             // slots per ring
 constexpr int P_VBASE = P_NS * P_TILE_BYTES;        // value ring after the key ring
-constexpr size_t ATTN_SMEM = 2 * P_NS * P_TILE_BYTES;  // 64 KiB
+constexpr size_t ATTN_SMEM = 2 * P_NS * P_TILE_BYTES;  // 128 KiB
 constexpr float LAZY_LOG2 = 16.0f;                  // log2 of the largest row sum left unrescaled
 
 template <int N>
@@ -410,6 +413,8 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
   load_v(0, ic<0>());
   load_k(min(3, last_t), ic<3>());
   load_v(min(1, last_t), ic<1>());
+  load_k(min(4, last_t), ic<4>());
+  load_v(min(2, last_t), ic<2>());
 
   // Queries: B operand of S^T = K Q^T.  The lane holds query row l32 and dims
   // 16*ks + 8*g .. +7, rotated in fp32, scaled by the row's power-of-two
@@ -565,8 +570,8 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     constexpr int b = t4 & 1;
     constexpr bool do_qk = decltype(QK)::value != 0;
     constexpr bool do_pv = decltype(PV)::value != 0;
-    constexpr ic<(t4 + 1) & 3> kslot{};  // K(t+1)
-    constexpr ic<(t4 + 3) & 3> vslot{};  // V(t-1)
+    constexpr ic<(t4 + 1) & 7> kslot{};  // K(t+1)
+    constexpr ic<(t4 + 7) & 7> vslot{};  // V(t-1)
     u32x4 kf[8];
     bf16x8 vf[8];
     float ep0 = 0.0f, ep1 = 0.0f;
@@ -604,35 +609,36 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     if (do_qk) sc[1 - b] = acc;
   };
 
-  // Steady iteration t (1 <= t <= last_t - 1), T4 = t mod 4.  Loads K(t+4)
-  // into the slot of K(t) and V(t+2) into the slot of V(t-2), both read for
-  // the last time in iteration t-1.  Past the last tile the index is
-  // clamped: the duplicate goes to a slot that is not read again, and every
-  // iteration keeps issuing exactly two loads, which the ring barrier counts.
-  auto step = [&](auto T4, int t) __attribute__((always_inline)) {
-    constexpr int t4 = decltype(T4)::value;
-    load_k(min(t + 4, last_t), ic<t4>());
-    load_v(min(t + 2, last_t), ic<(t4 + 2) & 3>());
+  // Steady iteration t (1 <= t <= last_t - 1), T8 = t mod 8.  Loads K(t+5)
+  // and V(t+3).  Iterations pair up into epochs (t odd, t+1) that end with
+  // one barrier: within an epoch no slot that is read is also written, and
+  // everything an epoch reads was issued at least two epochs earlier.  Past
+  // the last tile the index is clamped: the duplicate goes to a slot that is
+  // not read again, and every iteration keeps issuing the same loads, which
+  // the ring barrier counts.
+  auto step = [&](auto T8, int t) __attribute__((always_inline)) {
+    constexpr int t8 = decltype(T8)::value;
     u32x4 pw[2];
     float rs;
-    region(T4, ic<1>(), ic<1>(), pw, rs);
-    settle(ic<t4 & 1>(), pw, rs);
+    region(T8, ic<1>(), ic<1>(), pw, rs);
+    load_k(min(t + 5, last_t), ic<(t8 + 5) & 7>());
+    load_v(min(t + 3, last_t), ic<(t8 + 3) & 7>());
+    settle(ic<t8 & 1>(), pw, rs);
     ct = cq * ksc[(t + 1) >> 1];
-    ring_barrier<4>();  // K(t+2) and V(t), issued in iteration t-2, have landed
+    if ((t8 & 1) == 0) ring_barrier<4>();  // end of an epoch: its loads may stay in flight
   };
   // Last iteration t = last_t >= 1: exponentials of tile t and products of
   // tile t-1, then the products of tile t.
-  auto last = [&](auto T4) __attribute__((always_inline)) {
-    constexpr int t4 = decltype(T4)::value;
-    if (ragged) mask_tail(ic<t4 & 1>(), last_t);
+  auto last = [&](auto T8) __attribute__((always_inline)) {
+    constexpr int t8 = decltype(T8)::value;
+    if (ragged) mask_tail(ic<t8 & 1>(), last_t);
     u32x4 pw[2];
     float rs;
-    region(T4, ic<0>(), ic<1>(), pw, rs);
-    settle(ic<t4 & 1>(), pw, rs);
+    region(T8, ic<0>(), ic<1>(), pw, rs);
+    settle(ic<t8 & 1>(), pw, rs);
     ring_barrier<0>();  // V(t) has landed
-    pv_alone(ic<t4 & 1>(), ic<t4>());
+    pv_alone(ic<t8 & 1>(), ic<t8>());
   };
-
   qk_alone(ic<0>(), ic<0>());
   if (n_kt == 1) {
     if (ragged) mask_tail(ic<0>(), 0);
@@ -643,42 +649,49 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     ring_barrier<0>();
     pv_alone(ic<0>(), ic<0>());
   } else {
-    ring_barrier<4>();  // every wave is done with K(0) before its slot is refilled
+    ring_barrier<6>();  // every wave is done with K(0) before its slot is refilled
     {
-      // t = 0: no products of an earlier tile yet.
-      load_k(min(4, last_t), ic<0>());
-      load_v(min(2, last_t), ic<2>());
+      // t = 0: no products of an earlier tile yet; an epoch of its own.
       u32x4 pw[2];
       float rs;
       region(ic<0>(), ic<1>(), ic<0>(), pw, rs);
+      load_k(min(5, last_t), ic<5>());
+      load_v(min(3, last_t), ic<3>());
       settle(ic<0>(), pw, rs);
       ct = cq * ksc[1 >> 1];
       ring_barrier<4>();
     }
     int t = 1;
-    for (; t + 3 <= last_t - 1; t += 4) {
+    for (; t + 7 <= last_t - 1; t += 8) {
       step(ic<1>(), t);
       step(ic<2>(), t + 1);
       step(ic<3>(), t + 2);
-      step(ic<0>(), t + 3);
+      step(ic<4>(), t + 3);
+      step(ic<5>(), t + 4);
+      step(ic<6>(), t + 5);
+      step(ic<7>(), t + 6);
+      step(ic<0>(), t + 7);
     }
-    if (t <= last_t - 1) {
-      step(ic<1>(), t);
-      ++t;
-      if (t <= last_t - 1) {
-        step(ic<2>(), t);
-        ++t;
-        if (t <= last_t - 1) {
-          step(ic<3>(), t);
-          ++t;
-        }
-      }
-    }
-    switch (last_t & 3) {
+    // Up to seven more steps, continuing the t mod 8 sequence 1, 2, ..., 7.
+    if (t <= last_t - 1) { step(ic<1>(), t); ++t;
+    if (t <= last_t - 1) { step(ic<2>(), t); ++t;
+    if (t <= last_t - 1) { step(ic<3>(), t); ++t;
+    if (t <= last_t - 1) { step(ic<4>(), t); ++t;
+    if (t <= last_t - 1) { step(ic<5>(), t); ++t;
+    if (t <= last_t - 1) { step(ic<6>(), t); ++t;
+    if (t <= last_t - 1) { step(ic<7>(), t); ++t; } } } } } } }
+    // The last iteration starts a new epoch when t is odd; when t is even
+    // its epoch partner (t - 1) ended without a barrier, and the one in
+    // last() closes it.
+    switch (last_t & 7) {
       case 0: last(ic<0>()); break;
       case 1: last(ic<1>()); break;
       case 2: last(ic<2>()); break;
-      default: last(ic<3>()); break;
+      case 3: last(ic<3>()); break;
+      case 4: last(ic<4>()); break;
+      case 5: last(ic<5>()); break;
+      case 6: last(ic<6>()); break;
+      default: last(ic<7>()); break;
     }
   }
 
