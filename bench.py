@@ -103,6 +103,58 @@ def cpu_baseline(c, flop_per_row_head, target_seconds=15.0):
                       f"({t_used:.1f} s of float64 oracle time; FLOP counted as 4*S*d per row and head)"}
 
 
+def survey_workload(name, steps, warmup):
+    """Time one workload: the whole path, the attention kernel alone and the standalone RoPE kernel."""
+    import numpy as np
+    import torch
+
+    from joint_sequence_attention_amd import h3attn as H
+    from joint_sequence_attention_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    cfg = wl.config(name)
+    cu, pos = H.h3attn_build_layout(cfg["segments"])
+    N, heads = int(cu[-1]), cfg["heads"]
+    lens = np.diff(cu.astype(np.int64))
+    max_seqlen = int(lens.max())
+    qb, kb, vb = wl.random_qkv(N, heads, cfg["seed"])
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    cu_d = torch.from_numpy(cu).to(dev)
+    pos_d = torch.from_numpy(np.ascontiguousarray(pos)).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((heads, N), dtype=torch.float32, device=dev)
+    ws = H.alloc_workspace(N, heads, len(lens), dev)
+    y = torch.empty_like(q)
+    flop = H.attention_flops(cu, heads)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    step_ms = timed(lambda: H.h3attn_varlen_fwd(q, k, v, cu_d, pos_d, max_seqlen, out=out, lse=lse, workspace=ws))
+    H.h3attn_varlen_kv_prologue(k, v, cu_d, pos_d, max_seqlen, ws)
+    attn_ms = timed(lambda: H.h3attn_varlen_attention(q, cu_d, pos_d, max_seqlen, ws, out=out, lse=lse))
+    rope_ms = timed(lambda: H.h3attn_rope_apply(q, pos_d, out=y))
+    rope_bytes = 2 * N * heads * 128 * 2 + N * 12
+    return {"workload": name, "tokens": N, "heads": heads, "segments": int(len(lens)), "flop": flop,
+            "step_ms": round(step_ms, 4), "step_tflops": round(flop / step_ms / 1e9, 1),
+            "attn_ms": round(attn_ms, 4), "attn_tflops": round(flop / attn_ms / 1e9, 1),
+            "attn_pct_of_peak": round(100 * flop / attn_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "rope_apply_ms": round(rope_ms, 4), "rope_apply_gbps": round(rope_bytes / rope_ms / 1e6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +165,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="instead of the benchmark line, time every workload and the standalone RoPE kernel "
+                         "and print one JSON line each")
     args = ap.parse_args()
 
     if args.copy_calibration_mib:
@@ -140,6 +195,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.all_workloads:
+        for name in wl.CONFIG_ORDER:
+            print(json.dumps(survey_workload(name, args.steps, args.warmup)), flush=True)
+        return
     dev = torch.device("cuda:0")
     name = args.workload
     cfg = wl.config(name)
