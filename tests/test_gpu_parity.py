@@ -234,3 +234,41 @@ def test_reordered_references_change_output(gpu):
     o2, _ = c2.run()
     # same token values, different positions: outputs differ by far more than 1e-2 somewhere
     assert np.abs(device_to_f64(o1) - device_to_f64(o2)).max() > 5e-2
+
+
+# ---- limits of the launch shape --------------------------------------------------------------
+
+
+def test_long_single_segment_sampled_rows(gpu):
+    # One 262,144-token segment (twice the 1344x768 sequence): 1,024 query tiles, 8,192 key tiles
+    # per workgroup, token offsets past 2^25 elements.
+    segs = [[wl.visual(64, 64, 64)]]
+    c = Case(segs, 1, seed=71)
+    say(f"long segment: N={c.N} H=1")
+    out, lse = c.run()
+    out64, lse64 = device_to_f64(out), device_to_f64(lse)
+    assert np.all(np.isfinite(out64)) and np.all(np.isfinite(lse64))
+    rows = c.sample_rows(n_random=24, seed=71)
+    o_ref, l_ref = c.oracle_rows(rows)
+    compare(out64[rows], lse64[:, rows], o_ref, l_ref, label=f"long segment ({len(rows)} rows)")
+
+
+def test_two_thousand_short_segments_full(gpu):
+    # 2,000 segments of 0..64 tokens (grid y = 2,000; most tiles ragged, some segments empty).
+    rng = np.random.default_rng(72)
+    lengths = rng.integers(0, 65, size=2000)
+    segs = [[wl.visual(1, 1, int(n))] if n else [] for n in lengths]
+    c = Case(segs, 2, seed=72)
+    say(f"2000 segments: N={c.N} H=2, empty={int((lengths == 0).sum())}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="2000 segments")
+
+
+def test_many_heads_full(gpu):
+    # 128 heads on a 512-token sequence (grid z = 128; per-token stride 128 x 128 x 2 bytes).
+    c = Case([[wl.visual(2, 16, 16)]], 128, seed=73)
+    say(f"128 heads: N={c.N} H=128")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="128 heads")
