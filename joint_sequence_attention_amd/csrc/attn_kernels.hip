@@ -8,7 +8,8 @@
 // turned by a rotary embedding of their (t, h, w) position.
 //
 // Three kernels:
-//   rope_apply_kernel   y = rope(x): one 16-byte chunk (8 dims) per thread.
+//   rope_apply_kernel   y = rope(x): one 16-byte chunk position (8 dims) per
+//                       thread, applied to every head of the token.
 //   kv_prologue_kernel  rotates K once per call and packs it, with V
 //                       transposed, into 64-key tiles that start on a 64-key
 //                       boundary for every segment.  HBM-bound.
@@ -131,25 +132,41 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   return v;
 }
 
-// Rotate 4 consecutive pairs (dims 2*pair0 .. 2*pair0+7) in fp32.  Pair p
-// turns by phi = pos[axis(p)] * omega(p); (x0, x1) -> (x0 cos - x1 sin,
-// x0 sin + x1 cos).  Every caller goes through this one function, so the
-// standalone RoPE and the rotation fused into the attention loads round
-// identically.
-__device__ __forceinline__ void rope8(float (&x)[8], int pair0, const float* s_omega, const int* s_axis,
-                                      float pt, float ph, float pw) {
+// Rotation of 4 consecutive pairs (dims 2*pair0 .. 2*pair0+7) in fp32.  Pair
+// p turns by phi = pos[axis(p)] * omega(p); (x0, x1) -> (x0 cos - x1 sin,
+// x0 sin + x1 cos).  The angles depend on the token only, not on the head.
+// Every caller goes through these two functions, so the standalone RoPE and
+// the rotations fused into the attention path round identically.
+struct Rot4 {
+  float sn[4], cs[4];
+};
+
+__device__ __forceinline__ Rot4 rope_angles4(int pair0, const float* s_omega, const int* s_axis, float pt, float ph,
+                                             float pw) {
+  Rot4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = pair0 + i;
     const int ax = s_axis[p];
     const float ps = ax == 0 ? pt : (ax == 1 ? ph : pw);
     const float phi = ps * s_omega[p];
-    float sn, cs;
-    sincosf(phi, &sn, &cs);
-    const float x0 = x[2 * i], x1 = x[2 * i + 1];
-    x[2 * i] = fmaf(x0, cs, -(x1 * sn));
-    x[2 * i + 1] = fmaf(x0, sn, x1 * cs);
+    sincosf(phi, &r.sn[i], &r.cs[i]);
   }
+  return r;
+}
+
+__device__ __forceinline__ void rope_turn4(float (&x)[8], const Rot4& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = x[2 * i], x1 = x[2 * i + 1];
+    x[2 * i] = fmaf(x0, r.cs[i], -(x1 * r.sn[i]));
+    x[2 * i + 1] = fmaf(x0, r.sn[i], x1 * r.cs[i]);
+  }
+}
+
+__device__ __forceinline__ void rope8(float (&x)[8], int pair0, const float* s_omega, const int* s_axis,
+                                      float pt, float ph, float pw) {
+  rope_turn4(x, rope_angles4(pair0, s_omega, s_axis, pt, ph, pw));
 }
 
 __device__ __forceinline__ void stage_rope_table(const RopeTable& tab, float* s_omega, int* s_axis) {
@@ -163,19 +180,39 @@ __device__ __forceinline__ void stage_rope_table(const RopeTable& tab, float* s_
 // Standalone RoPE.  x and y may be the same buffer.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rope_apply_kernel(const u32x4* x, u32x4* y, const float* __restrict__ pos,
-                                                         int64_t n_chunks, int32_t chunks_per_token, RopeTable tab) {
+                                                         int64_t n_tokens, int32_t n_heads, RopeTable tab) {
+  // Thread (token, c): chunk c (dims 8c .. 8c+7) of every head of the token.
+  // The four angles are computed once and applied to all heads.
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
   stage_rope_table(tab, s_omega, s_axis);
   __syncthreads();
+  const int64_t n_items = n_tokens * CHUNKS_PER_ROW;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
-    const int64_t tok = c / chunks_per_token;
-    const int pair0 = int(c % CHUNKS_PER_ROW) * 4;
-    float f[8];
-    unpack8(x[c], f);
-    rope8(f, pair0, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
-    y[c] = pack8(f);
+  for (int64_t it = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; it < n_items; it += stride) {
+    const int64_t tok = it / CHUNKS_PER_ROW;
+    const int c = int(it % CHUNKS_PER_ROW);
+    const Rot4 r = rope_angles4(c * 4, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
+    const int64_t base = tok * n_heads * CHUNKS_PER_ROW + c;
+    int h = 0;
+    for (; h + 4 <= n_heads; h += 4) {  // four loads in flight before any use
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = x[base + int64_t(h + j) * CHUNKS_PER_ROW];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float f[8];
+        unpack8(v[j], f);
+        rope_turn4(f, r);
+        y[base + int64_t(h + j) * CHUNKS_PER_ROW] = pack8(f);
+      }
+    }
+    for (; h < n_heads; ++h) {
+      float f[8];
+      unpack8(x[base + int64_t(h) * CHUNKS_PER_ROW], f);
+      rope_turn4(f, r);
+      y[base + int64_t(h) * CHUNKS_PER_ROW] = pack8(f);
+    }
   }
 }
 
@@ -719,12 +756,11 @@ const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hip
 
 int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,
                       const RopeTable& table, void* stream) {
-  const int64_t n_chunks = n_tokens * n_heads * CHUNKS_PER_ROW;
-  int64_t blocks = (n_chunks + 255) / 256;
+  const int64_t n_items = n_tokens * CHUNKS_PER_ROW;
+  int64_t blocks = (n_items + 255) / 256;
   if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
   hipLaunchKernelGGL(rope_apply_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(x), static_cast<u32x4*>(y), pos, n_chunks,
-                     int32_t(n_heads * CHUNKS_PER_ROW), table);
+                     static_cast<const u32x4*>(x), static_cast<u32x4*>(y), pos, n_tokens, n_heads, table);
   return int(hipGetLastError());
 }
 
