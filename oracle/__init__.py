@@ -24,6 +24,9 @@ What it computes (sources are the pages the method is described on):
   encoding is rotary: "Day 0 Support ...", DiT property table).
 * ``attention`` -- exact softmax(Q~ K~^T / sqrt(d)) V per segment and head,
   plus the natural-log log-sum-exp of each row.
+* ``sage``    -- the lossy FP8 mode of the same attention: Q and K in e4m3
+  with one scale per query row and per 16 keys, P and V in e4m3 (vLLM-Omni
+  "MiniMax-H3" recipe, "Attention Backends", SAGE quantization).
 
 Every function is pinned by tests under ``tests/`` against closed forms,
 invariants, brute force and library routines (see ``tests/test_oracle_*.py``).
@@ -34,6 +37,7 @@ themselves rests on those pins and on the readings stated in each module.
 from .layout import layout, round_half_even
 from .rope import rope, rope_frequencies
 from .attention import attention, attention_rows
+from .sage import round_e4m3, sage_attention, sage_attention_rows
 
 __all__ = [
     "layout",
@@ -42,4 +46,7 @@ __all__ = [
     "rope_frequencies",
     "attention",
     "attention_rows",
+    "round_e4m3",
+    "sage_attention",
+    "sage_attention_rows",
 ]

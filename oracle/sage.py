@@ -1,0 +1,183 @@
+"""Oracle: block-quantized FP8 (e4m3) attention, the lossy "SAGE" mode, in float64.
+
+Test infrastructure only; see the package docstring.
+
+The vLLM-Omni "MiniMax-H3" recipe ("Attention Backends", the optional lossy
+optimizations of its datacenter-Blackwell backend) offers SAGE attention
+quantization for the long main DiT attention: Q and K in FP8 e4m3 with one
+scale per query token (query block size 1) and one scale per 16 keys (key
+block size 16), and P and V always in FP8.  It is lossy by design; the recipe
+asks to compare it against dense output before adopting it.
+
+The steps, in that order, with the readings taken where the page is silent:
+
+1. Rotate Q and K (``rope``), then hold the rotated values in float32, the
+   precision device arithmetic uses (the position contract in "MiniMax H3 on
+   Moore Threads MUSA", "MUSA validation").  Quantization decisions are taken
+   on those float32 values.
+2. Block scales are powers of two: a block with largest magnitude a gets
+   2**e with e the smallest integer for which a * 2**-e <= 448 (the largest
+   finite e4m3 value), limited to [-127, 127]; a block of zeros gets 2**0.
+   Reading: the page gives block sizes, not the scale format; power-of-two
+   scales keep the scaling exact and match the hardware's 8-bit exponent
+   block scales.
+3. Q: one block per (token, head) row of 128 dims.  K: per head, blocks of 16
+   consecutive keys counted from the first key of each segment (the last block
+   of a segment may be shorter).  V: per head, blocks of 64 consecutive keys
+   from the segment start, all 128 dims (reading: the page says V is FP8 but
+   gives no V block size).  Each element is x8 = e4m3(x * 2**-e), rounded to
+   nearest even, and stands for x8 * 2**e.
+4. z = q8 k8^T * scale, exact softmax per row: m = max z, p = exp(z - m),
+   l = sum p, lse = m + ln l.
+5. P in FP8 (``quantize_p``): p8 = e4m3(p * 16) / 16, i.e. probabilities
+   relative to the row maximum, scaled by 2**4 so that values down to 2**-10
+   stay normal (reading: the page gives no P scale).  out = (p8 v8) / l.
+   A kernel that evaluates softmax online rounds its probabilities relative
+   to a running maximum instead, so its P rounding differs element by element;
+   both are draws of the same rounding noise, which the GPU tests bound.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .rope import rope
+
+E4M3_MAX = 448.0
+E4M3_MIN_NORMAL_EXP = -6          # smallest normal 2**-6
+E4M3_MANTISSA_BITS = 3
+Q_BLOCK = 1                        # query rows per scale
+K_BLOCK = 16                       # keys per scale
+V_BLOCK = 64                       # keys per scale (all dims)
+P_SCALE_LOG2 = 4                   # P is quantized as p * 2**4
+
+
+def round_e4m3(x) -> np.ndarray:
+    """Round float64 values to the nearest e4m3 (OCP "fn") value, ties to even.
+
+    e4m3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; normals from
+    2**-6 to 448, subnormals in steps of 2**-9.  Inputs must satisfy
+    |x| < 464 (the midpoint above 448); larger values have no finite encoding.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(~np.isfinite(a)) or np.any(a >= 464.0):
+        raise ValueError("value outside the finite e4m3 range")
+    _, e = np.frexp(a)                               # a = f * 2**e, f in [0.5, 1)
+    expo = np.maximum(e - 1, E4M3_MIN_NORMAL_EXP)    # binade of a, subnormals share the lowest one
+    ulp = np.ldexp(1.0, expo - E4M3_MANTISSA_BITS)
+    r = np.rint(a / ulp) * ulp                       # np.rint rounds half to even
+    r = np.minimum(r, E4M3_MAX)                      # 448 < a < 464 rounds down to 448
+    return np.copysign(r, x)
+
+
+def pow2_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax * 2**-e <= 448, limited to [-127, 127]; 0 for amax == 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    if np.any(amax < 0) or np.any(~np.isfinite(amax)):
+        raise ValueError("amax must be finite and >= 0")
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.ceil(np.log2(safe / E4M3_MAX)).astype(np.int64)
+    # log2 may land one off next to powers of two: step to the exact smallest e
+    e = np.where(np.ldexp(safe, -e) > E4M3_MAX, e + 1, e)
+    e = np.where(np.ldexp(safe, -(e - 1)) <= E4M3_MAX, e - 1, e)
+    e = np.where(amax > 0, e, 0)
+    return np.clip(e, -127, 127)
+
+
+def quantize_block(x) -> np.ndarray:
+    """Quantize one block (any shape) with its power-of-two scale; returns the values it stands for."""
+    x = np.asarray(x, dtype=np.float64)
+    e = int(pow2_scale_exponent(np.abs(x).max() if x.size else 0.0))
+    return np.ldexp(round_e4m3(np.ldexp(x, -e)), e)
+
+
+def quantize_rows(x) -> np.ndarray:
+    """Q-style quantization: one block per row of the last axis (any leading shape)."""
+    x = np.asarray(x, dtype=np.float64)
+    e = pow2_scale_exponent(np.abs(x).max(axis=-1))[..., None]
+    return np.ldexp(round_e4m3(np.ldexp(x, -e)), e)
+
+
+def quantize_key_blocks(x, block) -> np.ndarray:
+    """Quantize x [S, D] in blocks of ``block`` consecutive rows from row 0 (last block may be short)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    for r0 in range(0, x.shape[0], block):
+        out[r0:r0 + block] = quantize_block(x[r0:r0 + block])
+    return out
+
+
+def _to_f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def _quantized_segment_kv(kr_seg, v_seg):
+    """Per-head K (16-key blocks) and V (64-key blocks) of one segment, [S, H, D] each."""
+    kq = np.empty_like(kr_seg)
+    vq = np.empty_like(v_seg)
+    for h in range(kr_seg.shape[1]):
+        kq[:, h, :] = quantize_key_blocks(kr_seg[:, h, :], K_BLOCK)
+        vq[:, h, :] = quantize_key_blocks(v_seg[:, h, :], V_BLOCK)
+    return kq, vq
+
+
+def _segment_head(q8, k8, v8, scale, quantize_p):
+    z = (q8 @ k8.T) * scale
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    l = p.sum(axis=1, keepdims=True)
+    pw = np.ldexp(round_e4m3(np.ldexp(p, P_SCALE_LOG2)), -P_SCALE_LOG2) if quantize_p else p
+    out = (pw @ v8) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, theta=10000.0, dims=(32, 48, 48),
+                        scale=None, quantize_p=True):
+    """Block-quantized FP8 attention for selected query rows (all rows when ``rows`` is None).
+
+    Keys and values of a row's segment are always quantized whole, exactly as
+    for the full computation.  Returns (out float64 [R, len(heads), D],
+    lse float64 [len(heads), R]).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    pos = np.asarray(pos, dtype=np.float64)
+    if q.shape != k.shape or q.shape != v.shape or q.ndim != 3:
+        raise ValueError("q, k, v must share one [N, H, D] shape")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu[0] != 0 or cu[-1] != q.shape[0] or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must rise from 0 to N")
+    N, H, D = q.shape
+    heads = list(range(H)) if heads is None else [int(h) for h in heads]
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    seg_of = np.searchsorted(cu, rows, side="right") - 1
+    out = np.zeros((len(rows), len(heads), D), dtype=np.float64)
+    lse = np.zeros((len(heads), len(rows)), dtype=np.float64)
+    for s in np.unique(seg_of):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero(seg_of == s)[0]
+        kr = _to_f32(rope(np.asarray(k[a:b][:, heads, :], dtype=np.float64), pos[a:b], theta, dims))
+        vs = np.asarray(v[a:b][:, heads, :], dtype=np.float64)
+        kq, vq = _quantized_segment_kv(kr, vs)
+        qr = _to_f32(rope(np.asarray(q[rows[sel]][:, heads, :], dtype=np.float64), pos[rows[sel]], theta, dims))
+        qq = quantize_rows(qr)
+        for j in range(len(heads)):
+            for r0 in range(0, len(sel), 512):
+                part = sel[r0:r0 + 512]
+                o, l = _segment_head(qq[r0:r0 + 512, j, :], kq[:, j, :], vq[:, j, :], scale, quantize_p)
+                out[part, j, :] = o
+                lse[j, part] = l
+    return out, lse
+
+
+def sage_attention(q, k, v, cu_seqlens, pos, **kw):
+    """Full block-quantized FP8 attention: (out float64 [N, H, D], lse float64 [H, N])."""
+    out, lse = sage_attention_rows(q, k, v, cu_seqlens, pos, None, None, **kw)
+    return out, lse

@@ -1,0 +1,244 @@
+"""Pins for the oracle's block-quantized FP8 attention (the lossy "SAGE" mode).
+
+The e4m3 rounding is checked against torch's float8_e4m3fn conversion (an
+independent library routine) and against hand-worked values; the block scale
+against its closed form; the attention against the exact oracle on inputs that
+quantization leaves unchanged, against a brute-force loop, and against
+invariants that the block structure implies.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import sage
+
+D = 128
+
+
+def _e4m3_grid():
+    """All finite non-negative e4m3 values, from the encoding: codes 0 .. 126."""
+    vals = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals.append(math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7))
+    return np.array(vals)
+
+
+def test_e4m3_grid_closed_form():
+    g = _e4m3_grid()
+    assert g[0] == 0.0 and g[-1] == 448.0 and len(np.unique(g)) == 127
+    assert g[1] == 2.0 ** -9 and g[8] == 2.0 ** -6      # smallest subnormal, smallest normal
+    assert np.all(sage.round_e4m3(g) == g)              # every grid value is its own rounding
+    assert np.all(sage.round_e4m3(-g) == -g)
+
+
+def test_e4m3_hand_worked_values():
+    cases = {
+        1.0625: 1.0,          # midpoint of 1.0 (m=0) and 1.125 (m=1): ties to the even mantissa
+        1.1875: 1.25,         # midpoint of 1.125 (m=1) and 1.25 (m=2)
+        2.0 ** -10: 0.0,      # midpoint of 0 and the smallest subnormal
+        3 * 2.0 ** -10: 2.0 ** -8,
+        232.0: 224.0,         # midpoint of 224 (m=6) and 240 (m=7)
+        460.0: 448.0,
+        0.3: 0.3125,          # 0.3 = 1.2 * 2^-2 -> 1.25 * 2^-2
+        -5.1: -5.0,
+    }
+    for x, want in cases.items():
+        assert sage.round_e4m3(x) == want, (x, sage.round_e4m3(x), want)
+    with pytest.raises(ValueError):
+        sage.round_e4m3(464.0)
+
+
+def test_e4m3_matches_torch_float8():
+    g = _e4m3_grid()
+    mids = (g[:-1] + g[1:]) / 2
+    rng = np.random.default_rng(3)
+    near = np.concatenate([np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1000))]).astype(np.float64)
+    rand = np.ldexp(rng.uniform(0.5, 1.0, 20000), rng.integers(-14, 9, 20000))
+    x = np.concatenate([g, mids, near, rand[rand < 464.0]]).astype(np.float32).astype(np.float64)
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(sage.round_e4m3(x), ref)
+
+
+def test_pow2_scale_exponent_closed_form():
+    cases = {448.0: 0, 449.0: 1, 224.0: -1, 224.5: 0, 1.0: -8, 3.5: -7, 3.51: -6, 0.0: 0,
+             2.0 ** -200: -127, 896.0: 1, 896.5: 2}
+    for amax, e in cases.items():
+        assert int(sage.pow2_scale_exponent(amax)) == e, (amax, e)
+    rng = np.random.default_rng(4)
+    a = np.ldexp(rng.uniform(0.5, 1.0, 5000), rng.integers(-60, 60, 5000))
+    e = sage.pow2_scale_exponent(a)
+    assert np.all(np.ldexp(a, -e) <= 448.0)             # fits
+    assert np.all(np.ldexp(a, -(e - 1)) > 448.0)        # and is the smallest that fits
+    assert np.all((np.ldexp(a, -e) > 224.0))
+
+
+def test_quantize_block_properties():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((16, D)) * 3.0
+    qx = sage.quantize_block(x)
+    assert np.array_equal(sage.quantize_block(qx), qx)                  # idempotent
+    for j in (-9, -1, 3, 20):
+        assert np.array_equal(sage.quantize_block(np.ldexp(x, j)), np.ldexp(qx, j))  # power-of-two equivariant
+    e = int(sage.pow2_scale_exponent(np.abs(x).max()))
+    normal = np.abs(x) >= math.ldexp(1.0, e - 6)
+    rel = np.abs(qx - x)[normal] / np.abs(x)[normal]
+    assert rel.max() <= 2.0 ** -4                                       # half an ulp of a 3-bit mantissa
+    assert 224.0 < np.abs(qx).max() * 2.0 ** -e <= 448.0
+
+
+def test_key_blocks_start_at_row_zero_and_are_independent():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((40, D))
+    base = sage.quantize_key_blocks(x, 16)
+    y = x.copy()
+    y[17, 5] = 1000.0                                   # a large value in the second block (rows 16..31)
+    got = sage.quantize_key_blocks(y, 16)
+    assert np.array_equal(got[:16], base[:16]) and np.array_equal(got[32:], base[32:])
+    assert not np.array_equal(got[16:32], base[16:32])
+    assert np.array_equal(got[32:], sage.quantize_block(x[32:]))        # the short last block stands alone
+
+
+def _exact_inputs(n, h, seed):
+    """Inputs that the block quantization leaves unchanged: e4m3 values whose every block holds 448."""
+    rng = np.random.default_rng(seed)
+    g = _e4m3_grid()
+    pick = lambda shape: g[rng.integers(0, 127, shape)] * rng.choice([-1.0, 1.0], shape)
+    q, k, v = pick((n, h, D)), pick((n, h, D)), pick((n, h, D))
+    q[:, :, 0] = 448.0
+    for r0 in range(0, n, 16):
+        k[r0, :, 0] = 448.0
+    for r0 in range(0, n, 64):
+        v[r0, :, 0] = 448.0
+    return q / 64.0, k / 64.0, v            # scales 2^-6: the block maxima become 7, still exact
+
+
+def test_sage_equals_exact_attention_when_quantization_is_exact():
+    n, h = 150, 2
+    q, k, v = _exact_inputs(n, h, 7)
+    pos = np.zeros((n, 3))                  # identity rotation
+    cu = np.array([0, n])
+    out_s, lse_s = sage.sage_attention(q, k, v, cu, pos, quantize_p=False)
+    out_e, lse_e = oracle.attention(q, k, v, cu, pos)
+    assert np.max(np.abs(out_s - out_e)) <= 1e-12 * np.max(np.abs(out_e))
+    assert np.max(np.abs(lse_s - lse_e)) <= 1e-12 * np.max(np.abs(lse_e))
+
+
+def test_sage_p_rounding_stays_within_its_bound():
+    n, h = 150, 2
+    q, k, v = _exact_inputs(n, h, 8)
+    q = q / 8.0                              # softer scores: many probabilities well below the maximum
+    pos = np.zeros((n, 3))
+    cu = np.array([0, n])
+    out_p, lse_p = sage.sage_attention(q, k, v, cu, pos, quantize_p=True)
+    out_u, lse_u = sage.sage_attention(q, k, v, cu, pos, quantize_p=False)
+    assert np.array_equal(lse_p, lse_u)                # the row sums use unrounded probabilities
+    z = (q[:, 0] @ k[:, 0].T) / math.sqrt(D)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    # per probability: half an e4m3 ulp relative, or half the subnormal step (2^-10 / 16) absolute
+    err_p = np.maximum(p * 2.0 ** -4, 2.0 ** -14)
+    bound = (err_p @ np.abs(v[:, 0])) / p.sum(axis=1, keepdims=True)
+    assert np.all(np.abs(out_p[:, 0] - out_u[:, 0]) <= bound * (1 + 1e-12))
+    assert np.max(np.abs(out_p - out_u)) > 0           # P rounding is really applied
+
+
+def _brute_sage(q, k, v, cu, scale):
+    """Loops over segment, head and query row; quantization from the block definition, written out."""
+    N, H, _ = q.shape
+    out = np.zeros((N, H, D))
+    lse = np.zeros((H, N))
+
+    def qblock(x):
+        amax = max(abs(t) for t in x.ravel())
+        e = 0
+        if amax > 0:
+            e = -127
+            while amax * 2.0 ** -e > 448.0:
+                e += 1
+        return np.array([float(sage.round_e4m3(t * 2.0 ** -e)) * 2.0 ** e for t in x.ravel()]).reshape(x.shape)
+
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            continue
+        for h in range(H):
+            kq = np.concatenate([qblock(k[j:min(j + 16, b), h]) for j in range(a, b, 16)])
+            vq = np.concatenate([qblock(v[j:min(j + 64, b), h]) for j in range(a, b, 64)])
+            for i in range(a, b):
+                qq = qblock(q[i, h])
+                z = [sum(qq[d] * kq[j][d] for d in range(D)) * scale for j in range(b - a)]
+                zm = max(z)
+                p = [math.exp(t - zm) for t in z]
+                tot = sum(p)
+                pq = [float(sage.round_e4m3(t * 16.0)) / 16.0 for t in p]
+                for d in range(D):
+                    out[i, h, d] = sum(pq[j] * vq[j][d] for j in range(b - a)) / tot
+                lse[h, i] = zm + math.log(tot)
+    return out, lse
+
+
+def test_sage_matches_brute_force():
+    rng = np.random.default_rng(9)
+    cu = np.array([0, 5, 5, 75])            # an empty segment and one that spans several blocks
+    n, h = 75, 2
+    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
+    q, k, v = (x.astype(np.float32).astype(np.float64) for x in (q, k, v))
+    pos = np.zeros((n, 3))
+    out, lse = sage.sage_attention(q, k, v, cu, pos)
+    bo, bl = _brute_sage(q, k, v, cu, 1.0 / math.sqrt(D))
+    assert np.max(np.abs(out - bo)) <= 1e-12
+    assert np.max(np.abs(lse - bl)) <= 1e-12
+
+
+def test_sage_segment_isolation_and_row_independence():
+    rng = np.random.default_rng(10)
+    lens = [37, 70, 21]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    n, h = int(cu[-1]), 2
+    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
+    pos = np.stack([rng.integers(0, 5, n), rng.integers(0, 9, n), rng.integers(0, 9, n)], axis=1).astype(float)
+    out, lse = sage.sage_attention(q, k, v, cu, pos)
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        o1, l1 = sage.sage_attention(q[a:b], k[a:b], v[a:b], np.array([0, b - a]), pos[a:b])
+        assert np.array_equal(o1, out[a:b]) and np.array_equal(l1, lse[:, a:b])
+    q2 = q.copy()
+    q2[40] *= 1000.0                        # another query row's magnitude: its own block only
+    o2, l2 = sage.sage_attention(q2, k, v, cu, pos)
+    keep = np.arange(n) != 40
+    assert np.array_equal(o2[keep], out[keep]) and np.array_equal(l2[:, keep], lse[:, keep])
+    rows = np.array([0, 36, 37, 80, 106, 127])
+    orow, lrow = sage.sage_attention_rows(q, k, v, cu, pos, rows)
+    assert np.array_equal(orow, out[rows]) and np.array_equal(lrow, lse[:, rows])
+
+
+def test_sage_value_scaling_is_exact():
+    rng = np.random.default_rng(11)
+    n, h = 90, 1
+    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
+    pos = np.zeros((n, 3))
+    cu = np.array([0, n])
+    out, _ = sage.sage_attention(q, k, v, cu, pos)
+    out2, _ = sage.sage_attention(q, k, np.ldexp(v, 7), cu, pos)
+    assert np.array_equal(out2, np.ldexp(out, 7))
+
+
+def test_sage_close_to_exact_on_the_tiny_workload():
+    from joint_sequence_attention_amd import workloads as wl
+    cfg = wl.config("tiny")
+    cu, pos = oracle.layout(cfg["segments"])
+    n = int(cu[-1])
+    qb, kb, vb = wl.random_qkv(n, cfg["heads"], cfg["seed"])
+    q, k, v = (wl.bf16_bits_to_f32(b).astype(np.float64) for b in (qb, kb, vb))
+    out_s, lse_s = sage.sage_attention(q, k, v, cu, pos)
+    out_e, lse_e = oracle.attention(q, k, v, cu, pos)
+    # lossy, but not far: 3-bit mantissas on every operand
+    assert np.max(np.abs(lse_s - lse_e)) < 0.05
+    assert np.max(np.abs(out_s - out_e)) < 0.1
+    assert np.mean(np.abs(out_s - out_e)) < 0.01
