@@ -166,6 +166,51 @@ h3attn_status h3attn_varlen_attention(const void* q, const int32_t* cu_seqlens, 
                                       const h3attn_rope_cfg* rope, const void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/* ---------------------------------------------------------------------
+ * Lossy FP8 mode of the same attention ("SAGE" quantization).
+ *
+ * Defined by the vLLM-Omni "MiniMax-H3" recipe, section "Attention
+ * Backends": for the long main DiT attention, queries and keys are quantized
+ * to FP8 e4m3 with one scale per query token and one scale per 16 keys, and
+ * probabilities and values are FP8 as well.  The recipe marks it lossy and
+ * asks for a comparison against dense output before use.
+ *
+ * Here: rotated queries and keys (fp32) are scaled per block by a power of
+ * two (the smallest that brings the block's largest magnitude to <= 448) and
+ * rounded to nearest e4m3; one block is a (token, head) row of q, or 16
+ * consecutive keys of one head counted from its segment's first key.  Values
+ * are scaled per 64 consecutive keys of one head and rounded likewise.
+ * Probabilities enter the second contraction as e4m3 of p * 2^4 relative to
+ * a running maximum; row sums and all accumulation are fp32; out is bf16 and
+ * lse fp32 exactly as for h3attn_varlen_fwd, whose argument meanings, layout,
+ * ownership and error rules apply unchanged.  Only the workspace differs:
+ * it must hold h3attn_varlen_fwd_fp8_workspace_size bytes (256-byte aligned)
+ * and its contents on return are unspecified.
+ * ------------------------------------------------------------------- */
+size_t h3attn_varlen_fwd_fp8_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs);
+
+h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                    const float* pos_thw, void* out, float* lse, int64_t n_tokens, int32_t n_heads,
+                                    int32_t head_dim, int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
+                                    const h3attn_rope_cfg* rope, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* The two stages of h3attn_varlen_fwd_fp8, with the same contract as the
+ * exact mode's pair: kv_prologue_fp8 rotates k, quantizes k and v and packs
+ * them into the workspace; attention_fp8 rotates and quantizes q as it loads
+ * it and reads k and v only through the workspace. */
+h3attn_status h3attn_varlen_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu_seqlens,
+                                            const float* pos_thw, int64_t n_tokens, int32_t n_heads,
+                                            int32_t head_dim, int32_t n_seqs, int32_t max_seqlen,
+                                            const h3attn_rope_cfg* rope, void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqlens, const float* pos_thw, void* out,
+                                          float* lse, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                          int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
+                                          const h3attn_rope_cfg* rope, const void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Status name ("H3ATTN_OK", ...); never NULL. */
 const char* h3attn_status_string(h3attn_status s);
 /* Reason for the last non-OK status returned on this thread ("" if none). */

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libh3attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "layout.cpp", "attn_kernels.hip"]
+SOURCES = ["api.cpp", "layout.cpp", "attn_kernels.hip", "attn_fp8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -70,22 +70,47 @@ size_t workspace_bytes_for(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
   return workspace_layout(n_tokens, n_heads, n_seqs).total;
 }
 
-h3attn_status check_workspace(const void* ws, size_t bytes, int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+h3attn_status check_workspace_size(const void* ws, size_t bytes, size_t need, const char* too_small) {
   if (!ws) return fail(H3ATTN_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(H3ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (bytes < workspace_bytes_for(n_tokens, n_heads, n_seqs))
-    return fail(H3ATTN_ERR_WORKSPACE, "workspace smaller than h3attn_varlen_fwd_workspace_size");
+  if (bytes < need) return fail(H3ATTN_ERR_WORKSPACE, too_small);
+  return H3ATTN_OK;
+}
+
+h3attn_status check_workspace(const void* ws, size_t bytes, int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
+  return check_workspace_size(ws, bytes, workspace_bytes_for(n_tokens, n_heads, n_seqs),
+                              "workspace smaller than h3attn_varlen_fwd_workspace_size");
+}
+
+h3attn_status check_workspace_fp8(const void* ws, size_t bytes, int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
+  return check_workspace_size(ws, bytes, workspace_layout_fp8(n_tokens, n_heads, n_seqs).total,
+                              "workspace smaller than h3attn_varlen_fwd_fp8_workspace_size");
+}
+
+// out and lse against q (and k, v when given), each other and the workspace.
+h3attn_status check_outputs(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* ws, size_t ws_bytes, int64_t n_tokens, int32_t n_heads, int32_t head_dim) {
+  const size_t nb = size_t(n_tokens) * n_heads * head_dim * 2;
+  const size_t nl = size_t(n_tokens) * n_heads * 4;
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (!in) continue;
+    if (overlaps(out, nb, in, nb) || overlaps(lse, nl, in, nb) || overlaps(ws, ws_bytes, in, nb))
+      return fail(H3ATTN_ERR_INVALID_ARG, "out, lse and workspace must not overlap the inputs");
+  }
+  if (overlaps(out, nb, lse, nl) || overlaps(out, nb, ws, ws_bytes) || overlaps(lse, nl, ws, ws_bytes))
+    return fail(H3ATTN_ERR_INVALID_ARG, "out, lse and workspace must not overlap each other");
   return H3ATTN_OK;
 }
 
 h3attn_status hip_status(int err) {
   if (err == 0) return H3ATTN_OK;
   return fail(H3ATTN_ERR_HIP, hip_error_string(err));
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
 }
 
 }  // namespace
@@ -231,6 +256,106 @@ h3attn_status h3attn_varlen_fwd(const void* q, const void* k, const void* v, con
                                    softmax_scale, rope, workspace, workspace_bytes, stream);
   } catch (...) {
     return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_fwd");
+  }
+}
+
+size_t h3attn_varlen_fwd_fp8_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs) {
+  if (n_tokens < 0 || n_heads < 1 || head_dim != kHeadDim || n_seqs < 1) return 0;
+  return workspace_layout_fp8(n_tokens, n_heads, n_seqs).total;
+}
+
+h3attn_status h3attn_varlen_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu_seqlens,
+                                            const float* pos_thw, int64_t n_tokens, int32_t n_heads,
+                                            int32_t head_dim, int32_t n_seqs, int32_t max_seqlen,
+                                            const h3attn_rope_cfg* rope, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  try {
+    clear_error();
+    h3attn_status st = check_varlen(n_tokens, n_heads, head_dim, n_seqs, max_seqlen);
+    if (st != H3ATTN_OK) return st;
+    RopeTable table;
+    st = make_rope_table(rope, head_dim, &table);
+    if (st != H3ATTN_OK) return st;
+    if (n_tokens == 0) return H3ATTN_OK;
+    if (!k || !v || !cu_seqlens || !pos_thw) return fail(H3ATTN_ERR_INVALID_ARG, "k, v, cu_seqlens and pos_thw must be non-NULL");
+    st = check_workspace_fp8(workspace, workspace_bytes, n_tokens, n_heads, n_seqs);
+    if (st != H3ATTN_OK) return st;
+    const size_t nb = size_t(n_tokens) * n_heads * head_dim * 2;
+    if (overlaps(workspace, workspace_bytes, k, nb) || overlaps(workspace, workspace_bytes, v, nb))
+      return fail(H3ATTN_ERR_INVALID_ARG, "workspace must not overlap k or v");
+    const int64_t rows = packed_rows(n_tokens, n_seqs);
+    const WorkspaceLayoutFp8 wl = workspace_layout_fp8(n_tokens, n_heads, n_seqs);
+    char* ws = static_cast<char*>(workspace);
+    return hip_status(launch_kv_prologue_fp8(k, v, cu_seqlens, pos_thw, n_heads, n_seqs, max_seqlen, table,
+                                             ws + wl.keys_offset, ws + wl.values_offset,
+                                             reinterpret_cast<unsigned*>(ws + wl.kscale_offset),
+                                             reinterpret_cast<unsigned*>(ws + wl.vscale_offset), rows, stream));
+  } catch (...) {
+    return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_kv_prologue_fp8");
+  }
+}
+
+h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqlens, const float* pos_thw, void* out,
+                                          float* lse, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                          int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
+                                          const h3attn_rope_cfg* rope, const void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  try {
+    clear_error();
+    h3attn_status st = check_varlen(n_tokens, n_heads, head_dim, n_seqs, max_seqlen);
+    if (st != H3ATTN_OK) return st;
+    RopeTable table;
+    st = make_rope_table(rope, head_dim, &table);
+    if (st != H3ATTN_OK) return st;
+    if (!std::isfinite(softmax_scale)) return fail(H3ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (n_tokens == 0) return H3ATTN_OK;
+    if (!q || !cu_seqlens || !pos_thw || !out || !lse)
+      return fail(H3ATTN_ERR_INVALID_ARG, "q, cu_seqlens, pos_thw, out and lse must be non-NULL");
+    st = check_workspace_fp8(workspace, workspace_bytes, n_tokens, n_heads, n_seqs);
+    if (st != H3ATTN_OK) return st;
+    st = check_outputs(q, nullptr, nullptr, out, lse, workspace, workspace_bytes, n_tokens, n_heads, head_dim);
+    if (st != H3ATTN_OK) return st;
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
+    const int64_t rows = packed_rows(n_tokens, n_seqs);
+    const WorkspaceLayoutFp8 wl = workspace_layout_fp8(n_tokens, n_heads, n_seqs);
+    const char* ws = static_cast<const char*>(workspace);
+    return hip_status(launch_attention_fp8(q, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, n_seqs, max_seqlen,
+                                           scale, table, ws + wl.keys_offset, ws + wl.values_offset,
+                                           reinterpret_cast<const unsigned*>(ws + wl.kscale_offset),
+                                           reinterpret_cast<const unsigned*>(ws + wl.vscale_offset), rows, stream));
+  } catch (...) {
+    return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_attention_fp8");
+  }
+}
+
+h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                    const float* pos_thw, void* out, float* lse, int64_t n_tokens, int32_t n_heads,
+                                    int32_t head_dim, int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
+                                    const h3attn_rope_cfg* rope, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  try {
+    clear_error();
+    // Check everything both stages need before launching the first one.
+    h3attn_status st = check_varlen(n_tokens, n_heads, head_dim, n_seqs, max_seqlen);
+    if (st != H3ATTN_OK) return st;
+    RopeTable table;
+    st = make_rope_table(rope, head_dim, &table);
+    if (st != H3ATTN_OK) return st;
+    if (!std::isfinite(softmax_scale)) return fail(H3ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (n_tokens == 0) return H3ATTN_OK;
+    if (!q || !k || !v || !cu_seqlens || !pos_thw || !out || !lse)
+      return fail(H3ATTN_ERR_INVALID_ARG, "q, k, v, cu_seqlens, pos_thw, out and lse must be non-NULL");
+    st = check_workspace_fp8(workspace, workspace_bytes, n_tokens, n_heads, n_seqs);
+    if (st != H3ATTN_OK) return st;
+    st = check_outputs(q, k, v, out, lse, workspace, workspace_bytes, n_tokens, n_heads, head_dim);
+    if (st != H3ATTN_OK) return st;
+    st = h3attn_varlen_kv_prologue_fp8(k, v, cu_seqlens, pos_thw, n_tokens, n_heads, head_dim, n_seqs, max_seqlen,
+                                       rope, workspace, workspace_bytes, stream);
+    if (st != H3ATTN_OK) return st;
+    return h3attn_varlen_attention_fp8(q, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, head_dim, n_seqs,
+                                       max_seqlen, softmax_scale, rope, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_fwd_fp8");
   }
 }
 

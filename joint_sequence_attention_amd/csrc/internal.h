@@ -51,7 +51,28 @@ inline WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_heads, int32
   return w;
 }
 
-// Kernel launchers (attn_kernels.hip).  They only enqueue; the caller has
+// FP8 workspace layout, in this order (every part 256-byte aligned):
+//   keys    e4m3 [H][rows][128]            rotated keys
+//   values  e4m3 [H][rows/64][128][64]     transposed 64-key tiles
+//   kscale  u32  [H][rows/64]              per tile: 4 exponent scales of 16 keys
+//   vscale  u32  [H][rows/64]              per tile: the exponent scale of its values
+struct WorkspaceLayoutFp8 {
+  size_t keys_offset, values_offset, kscale_offset, vscale_offset, total;
+};
+inline WorkspaceLayoutFp8 workspace_layout_fp8(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
+  const size_t rows = size_t(packed_rows(n_tokens, n_seqs));
+  const size_t plane = size_t(n_heads) * rows * kHeadDim;
+  const size_t scales = (size_t(n_heads) * (rows / kKeyTile) * 4 + 255) / 256 * 256;
+  WorkspaceLayoutFp8 w;
+  w.keys_offset = 0;
+  w.values_offset = plane;
+  w.kscale_offset = 2 * plane;
+  w.vscale_offset = 2 * plane + scales;
+  w.total = 2 * plane + 2 * scales;
+  return w;
+}
+
+// Kernel launchers (attn_kernels.hip, attn_fp8.hip).  They only enqueue; the caller has
 // validated every argument.  Return hipSuccess or the launch error.
 int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,
                       const RopeTable& table, void* stream);
@@ -62,6 +83,13 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
                      int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
                      const void* k_ws, const void* v_ws, const float* k_scale, int64_t rows_per_head,
                      void* stream);
+int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, const float* pos, int32_t n_heads,
+                           int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws, void* v_ws,
+                           unsigned* k_sc, unsigned* v_sc, int64_t rows_per_head, void* stream);
+int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
+                         int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
+                         const RopeTable& table, const void* k_ws, const void* v_ws, const unsigned* k_sc,
+                         const unsigned* v_sc, int64_t rows_per_head, void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace h3attn

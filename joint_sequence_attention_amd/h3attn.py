@@ -85,6 +85,14 @@ def lib():
     L.h3attn_varlen_attention.restype = ctypes.c_int
     L.h3attn_varlen_attention.argtypes = [vp, vp, vp, vp, vp, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.c_float, rp,
                                           vp, c_sz, vp]
+    L.h3attn_varlen_fwd_fp8_workspace_size.restype = c_sz
+    L.h3attn_varlen_fwd_fp8_workspace_size.argtypes = [c_i64, c_i32, c_i32, c_i32]
+    L.h3attn_varlen_fwd_fp8.restype = ctypes.c_int
+    L.h3attn_varlen_fwd_fp8.argtypes = list(L.h3attn_varlen_fwd.argtypes)
+    L.h3attn_varlen_kv_prologue_fp8.restype = ctypes.c_int
+    L.h3attn_varlen_kv_prologue_fp8.argtypes = list(L.h3attn_varlen_kv_prologue.argtypes)
+    L.h3attn_varlen_attention_fp8.restype = ctypes.c_int
+    L.h3attn_varlen_attention_fp8.argtypes = list(L.h3attn_varlen_attention.argtypes)
     _lib = L
     return L
 
@@ -97,6 +105,10 @@ EXPORTED = (
     "h3attn_varlen_fwd",
     "h3attn_varlen_kv_prologue",
     "h3attn_varlen_attention",
+    "h3attn_varlen_fwd_fp8_workspace_size",
+    "h3attn_varlen_fwd_fp8",
+    "h3attn_varlen_kv_prologue_fp8",
+    "h3attn_varlen_attention_fp8",
     "h3attn_status_string",
     "h3attn_last_error",
     "h3attn_abi_version",
@@ -202,9 +214,15 @@ def h3attn_varlen_fwd_workspace_size(n_tokens: int, n_heads: int, head_dim: int,
     return int(lib().h3attn_varlen_fwd_workspace_size(n_tokens, n_heads, head_dim, n_seqs))
 
 
-def alloc_workspace(n_tokens: int, n_heads: int, n_seqs: int, device=None):
+def h3attn_varlen_fwd_fp8_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_seqs: int) -> int:
+    return int(lib().h3attn_varlen_fwd_fp8_workspace_size(n_tokens, n_heads, head_dim, n_seqs))
+
+
+def alloc_workspace(n_tokens: int, n_heads: int, n_seqs: int, device=None, fp8: bool = False):
+    """Workspace for the exact path, or for the FP8 path with fp8=True (torch's allocation is 256-byte aligned)."""
     torch = _torch()
-    nbytes = h3attn_varlen_fwd_workspace_size(n_tokens, n_heads, 128, n_seqs)
+    size = h3attn_varlen_fwd_fp8_workspace_size if fp8 else h3attn_varlen_fwd_workspace_size
+    nbytes = size(n_tokens, n_heads, 128, n_seqs)
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device or "cuda")
 
 
@@ -274,6 +292,64 @@ def h3attn_varlen_attention(q, cu_seqlens, pos_thw, max_seqlen, workspace, out=N
                                          ctypes.byref(cfg), workspace.data_ptr(),
                                          workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
            "h3attn_varlen_attention")
+    return out, lse
+
+
+def h3attn_varlen_fwd_fp8(q, k, v, cu_seqlens, pos_thw, max_seqlen, out=None, lse=None, softmax_scale=0.0,
+                          theta=DEFAULT_THETA, dims=DEFAULT_DIMS, workspace=None, stream=None):
+    """Lossy FP8 (SAGE-style) mode of h3attn_varlen_fwd; same arguments and results."""
+    torch = _torch()
+    N, H, Dh, n_seqs = _varlen_common(q, cu_seqlens, pos_thw, max_seqlen)
+    _need(k, torch.bfloat16, q.shape, "k")
+    _need(v, torch.bfloat16, q.shape, "v")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    _need(out, torch.bfloat16, q.shape, "out")
+    _need(lse, torch.float32, (H, N), "lse")
+    if workspace is None:
+        workspace = alloc_workspace(N, H, n_seqs, q.device, fp8=True)
+    cfg = rope_cfg(theta, dims)
+    _check(lib().h3attn_varlen_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                       pos_thw.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, Dh, n_seqs,
+                                       int(max_seqlen), float(softmax_scale), ctypes.byref(cfg),
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream_ptr(stream)),
+           "h3attn_varlen_fwd_fp8")
+    return out, lse
+
+
+def h3attn_varlen_kv_prologue_fp8(k, v, cu_seqlens, pos_thw, max_seqlen, workspace, theta=DEFAULT_THETA,
+                                  dims=DEFAULT_DIMS, stream=None):
+    torch = _torch()
+    N, H, Dh, n_seqs = _varlen_common(k, cu_seqlens, pos_thw, max_seqlen)
+    _need(v, torch.bfloat16, k.shape, "v")
+    cfg = rope_cfg(theta, dims)
+    _check(lib().h3attn_varlen_kv_prologue_fp8(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                               pos_thw.data_ptr(), N, H, Dh, n_seqs, int(max_seqlen),
+                                               ctypes.byref(cfg), workspace.data_ptr(),
+                                               workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "h3attn_varlen_kv_prologue_fp8")
+    return workspace
+
+
+def h3attn_varlen_attention_fp8(q, cu_seqlens, pos_thw, max_seqlen, workspace, out=None, lse=None,
+                                softmax_scale=0.0, theta=DEFAULT_THETA, dims=DEFAULT_DIMS, stream=None):
+    torch = _torch()
+    N, H, Dh, n_seqs = _varlen_common(q, cu_seqlens, pos_thw, max_seqlen)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    _need(out, torch.bfloat16, q.shape, "out")
+    _need(lse, torch.float32, (H, N), "lse")
+    cfg = rope_cfg(theta, dims)
+    _check(lib().h3attn_varlen_attention_fp8(q.data_ptr(), cu_seqlens.data_ptr(), pos_thw.data_ptr(),
+                                             out.data_ptr(), lse.data_ptr(), N, H, Dh, n_seqs, int(max_seqlen),
+                                             float(softmax_scale), ctypes.byref(cfg), workspace.data_ptr(),
+                                             workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+           "h3attn_varlen_attention_fp8")
     return out, lse
 
 

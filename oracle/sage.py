@@ -35,6 +35,15 @@ The steps, in that order, with the readings taken where the page is silent:
    A kernel that evaluates softmax online rounds its probabilities relative
    to a running maximum instead, so its P rounding differs element by element;
    both are draws of the same rounding noise, which the GPU tests bound.
+
+Rounding decisions near a midpoint.  A kernel rotates in its own fp32
+arithmetic, within 2^-22 (1 + |phi|)(|x0| + |x1|) of the exact rotation
+(angle rounding, sin/cos and the multiply-adds); this oracle's float32 values
+are within a quarter of that.  Where a midpoint of the e4m3 grid (or a
+power-of-two boundary of a block scale) lies inside that window, both
+roundings are correct.  ``error_scales`` reports, per row, how far such
+elements can move lse and out (first order, with margin), so that a test can
+tell a valid alternative rounding from a wrong one.
 """
 
 from __future__ import annotations
@@ -110,21 +119,71 @@ def quantize_key_blocks(x, block) -> np.ndarray:
     return out
 
 
+ROTATION_ERROR = 2.0 ** -22          # fp32 rotation error coefficient (see the module docstring)
+
+
+def rotation_error_bound(x, pos, theta=10000.0, dims=(32, 48, 48)) -> np.ndarray:
+    """Per element of rope(x): 2^-22 (1 + |phi|)(|x0| + |x1|) over its rotation pair, float64 [N, H, D]."""
+    from .rope import rope_frequencies
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    pos = np.asarray(pos, dtype=np.float64)
+    out = np.empty_like(x)
+    offset = 0
+    for axis, width in enumerate(dims):
+        phi = pos[:, axis][:, None] * rope_frequencies(theta, width)[None, :]      # [N, width/2]
+        pair = x[:, :, offset:offset + width:2] + x[:, :, offset + 1:offset + width:2]
+        b = ROTATION_ERROR * (1.0 + np.abs(phi))[:, None, :] * pair
+        out[:, :, offset:offset + width:2] = b
+        out[:, :, offset + 1:offset + width:2] = b
+        offset += width
+    return out
+
+
+def quantize_block_margin(x, w):
+    """Quantize one block, and bound how much a rounding within +-w of each value could differ.
+
+    Returns (values the block stands for, change): change is 0 where every
+    value within +-w rounds the same way, else the largest move the other
+    rounding makes (one e4m3 step; for the whole block when its scale itself
+    could differ).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    a = float(np.abs(x).max()) if x.size else 0.0
+    wmax = float(w.max()) if w.size else 0.0
+    e = int(pow2_scale_exponent(a))
+    s = np.ldexp(x, -e)
+    r = round_e4m3(s)
+    q = np.ldexp(r, e)
+    if int(pow2_scale_exponent(max(a - wmax, 0.0))) != int(pow2_scale_exponent(a + wmax)):
+        # the block scale may be 2^(e-1) or 2^(e+1): every value may move by a step at the coarser scale
+        change = np.abs(x) * 2.0 ** -3 + np.ldexp(1.0, e + 1 - 9)
+        return q, change
+    ws = np.ldexp(w, -e)
+    lo = round_e4m3(s - ws)
+    hi = round_e4m3(s + ws)
+    change = np.ldexp(np.maximum(np.abs(lo - r), np.abs(hi - r)), e)
+    return q, change
+
+
 def _to_f32(x):
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def _quantized_segment_kv(kr_seg, v_seg):
-    """Per-head K (16-key blocks) and V (64-key blocks) of one segment, [S, H, D] each."""
+def _quantized_segment_kv(kr_seg, kw_seg, v_seg):
+    """Per-head K (16-key blocks, with rounding margins) and V (64-key blocks) of one segment, [S, H, D] each."""
     kq = np.empty_like(kr_seg)
+    kc = np.empty_like(kr_seg)
     vq = np.empty_like(v_seg)
     for h in range(kr_seg.shape[1]):
-        kq[:, h, :] = quantize_key_blocks(kr_seg[:, h, :], K_BLOCK)
+        for r0 in range(0, kr_seg.shape[0], K_BLOCK):
+            kq[r0:r0 + K_BLOCK, h], kc[r0:r0 + K_BLOCK, h] = quantize_block_margin(kr_seg[r0:r0 + K_BLOCK, h],
+                                                                                 kw_seg[r0:r0 + K_BLOCK, h])
         vq[:, h, :] = quantize_key_blocks(v_seg[:, h, :], V_BLOCK)
-    return kq, vq
+    return kq, kc, vq
 
 
-def _segment_head(q8, k8, v8, scale, quantize_p):
+def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None):
     z = (q8 @ k8.T) * scale
     m = z.max(axis=1, keepdims=True)
     p = np.exp(z - m)
@@ -132,16 +191,42 @@ def _segment_head(q8, k8, v8, scale, quantize_p):
     pw = np.ldexp(round_e4m3(np.ldexp(p, P_SCALE_LOG2)), -P_SCALE_LOG2) if quantize_p else p
     out = (pw @ v8) / l
     lse = m[:, 0] + np.log(l[:, 0])
-    return out, lse
+    # Spread of the P rounding: each probability moves by at most half an e4m3 ulp, 2^-4 of
+    # itself, or half the subnormal step, 2^-14 in these units; a rounding error spread evenly
+    # over that interval has standard deviation (bound) / sqrt(3).
+    e = np.maximum(p * 2.0 ** -4, 2.0 ** -(10 + P_SCALE_LOG2))
+    sigma = np.sqrt(((e * e) @ (v8 * v8)) / 3.0) / l
+    # Largest sum of absolute products behind one logit of the row: the scale of
+    # the rounding error any finite-precision evaluation of the row's scores has.
+    zabs = (np.abs(q8) @ np.abs(k8).T).max(axis=1) * abs(scale)
+    # Alternative roundings of elements next to a midpoint (qc, kc: how far each may move): the
+    # logits move by at most dz, lse by the probability-weighted dz, out by the weighted dz times
+    # the distance of v from out, plus the same for the lse shift (first order; 25 % margin).
+    if qc is None:
+        qc = np.zeros_like(q8)
+    if kc is None:
+        kc = np.zeros_like(k8)
+    dz = (np.abs(q8) @ kc.T + qc @ np.abs(k8).T) * abs(scale)
+    pd = p * dz
+    lse_flip = pd.sum(axis=1) / l[:, 0]
+    av = np.abs(v8)
+    ao = np.abs(out)
+    out_flip = (pd @ av + pd.sum(axis=1, keepdims=True) * ao + lse_flip[:, None] * (p @ av + l * ao)) / l
+    return out, lse, (sigma, zabs, 1.25 * lse_flip, 1.25 * out_flip)
 
 
 def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, theta=10000.0, dims=(32, 48, 48),
-                        scale=None, quantize_p=True):
+                        scale=None, quantize_p=True, error_scales=False):
     """Block-quantized FP8 attention for selected query rows (all rows when ``rows`` is None).
 
     Keys and values of a row's segment are always quantized whole, exactly as
     for the full computation.  Returns (out float64 [R, len(heads), D],
-    lse float64 [len(heads), R]).
+    lse float64 [len(heads), R]), and with ``error_scales`` also a dict with
+    "sigma", the standard deviation of ``out`` that rounding P to e4m3 causes,
+    float64 [R, len(heads), D]; "zabs", per row the largest
+    scale * sum_i |q8_i k8_i| over its keys, float64 [len(heads), R]; and
+    "lse_flip" [len(heads), R] and "out_flip" [R, len(heads), D], how far
+    alternative roundings next to a midpoint can move lse and out.
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -160,24 +245,41 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     seg_of = np.searchsorted(cu, rows, side="right") - 1
     out = np.zeros((len(rows), len(heads), D), dtype=np.float64)
     lse = np.zeros((len(heads), len(rows)), dtype=np.float64)
+    sig = np.zeros((len(rows), len(heads), D), dtype=np.float64)
+    zabs = np.zeros((len(heads), len(rows)), dtype=np.float64)
+    lflip = np.zeros((len(heads), len(rows)), dtype=np.float64)
+    oflip = np.zeros((len(rows), len(heads), D), dtype=np.float64)
     for s in np.unique(seg_of):
         a, b = int(cu[s]), int(cu[s + 1])
         sel = np.nonzero(seg_of == s)[0]
-        kr = _to_f32(rope(np.asarray(k[a:b][:, heads, :], dtype=np.float64), pos[a:b], theta, dims))
+        k_seg = np.asarray(k[a:b][:, heads, :], dtype=np.float64)
+        kr = _to_f32(rope(k_seg, pos[a:b], theta, dims))
+        kw = 2.0 * rotation_error_bound(k_seg, pos[a:b], theta, dims)
         vs = np.asarray(v[a:b][:, heads, :], dtype=np.float64)
-        kq, vq = _quantized_segment_kv(kr, vs)
-        qr = _to_f32(rope(np.asarray(q[rows[sel]][:, heads, :], dtype=np.float64), pos[rows[sel]], theta, dims))
-        qq = quantize_rows(qr)
+        kq, kc, vq = _quantized_segment_kv(kr, kw, vs)
+        q_rows = np.asarray(q[rows[sel]][:, heads, :], dtype=np.float64)
+        qr = _to_f32(rope(q_rows, pos[rows[sel]], theta, dims))
+        qw = 2.0 * rotation_error_bound(q_rows, pos[rows[sel]], theta, dims)
+        qq = np.empty_like(qr)
+        qc = np.empty_like(qr)
+        for i in range(qr.shape[0]):
+            for j in range(qr.shape[1]):
+                qq[i, j], qc[i, j] = quantize_block_margin(qr[i, j], qw[i, j])
         for j in range(len(heads)):
             for r0 in range(0, len(sel), 512):
                 part = sel[r0:r0 + 512]
-                o, l = _segment_head(qq[r0:r0 + 512, j, :], kq[:, j, :], vq[:, j, :], scale, quantize_p)
+                o, l, (sg, za, lf, of) = _segment_head(qq[r0:r0 + 512, j, :], kq[:, j, :], vq[:, j, :], scale,
+                                                        quantize_p, qc[r0:r0 + 512, j, :], kc[:, j, :])
                 out[part, j, :] = o
                 lse[j, part] = l
-    return out, lse
+                sig[part, j, :] = sg
+                zabs[j, part] = za
+                lflip[j, part] = lf
+                oflip[part, j, :] = of
+    scales = {"sigma": sig, "zabs": zabs, "lse_flip": lflip, "out_flip": oflip}
+    return (out, lse, scales) if error_scales else (out, lse)
 
 
 def sage_attention(q, k, v, cu_seqlens, pos, **kw):
-    """Full block-quantized FP8 attention: (out float64 [N, H, D], lse float64 [H, N])."""
-    out, lse = sage_attention_rows(q, k, v, cu_seqlens, pos, None, None, **kw)
-    return out, lse
+    """Full block-quantized FP8 attention: (out float64 [N, H, D], lse float64 [H, N]) (and the error scales)."""
+    return sage_attention_rows(q, k, v, cu_seqlens, pos, None, None, **kw)

@@ -70,6 +70,17 @@ class Case:
         torch.cuda.synchronize()
         return out, lse
 
+    def run_fp8(self, **kw):
+        import torch
+        out, lse = H.h3attn_varlen_fwd_fp8(self.q, self.k, self.v, self.cu_d, self.pos_d, self.max_seqlen, **kw)
+        torch.cuda.synchronize()
+        return out, lse
+
+    def sage_rows(self, rows=None, **kw):
+        """Block-quantized oracle with P unrounded, and its error scales: (out, lse, {"sigma", "zabs"})."""
+        return oracle.sage_attention_rows(widen(self.qb), widen(self.kb), widen(self.vb), self.cu, self.pos, rows,
+                                          quantize_p=False, error_scales=True, **kw)
+
     def oracle_full(self, **kw):
         return oracle.attention(widen(self.qb), widen(self.kb), widen(self.vb), self.cu, self.pos, **kw)
 
@@ -120,3 +131,68 @@ def ragged_segments():
         [wl.visual(2, 10, 14), wl.audio(20, 2, attached=True)],
         [wl.audio(2, 1.0, attached=False)],
     ]
+
+
+# Bar for the lossy FP8 mode.
+#
+# Against the block-quantized oracle (oracle.sage with P left unrounded), the
+# kernel differs by:
+#   * the e4m3 rounding of its probabilities: per output element a sum of
+#     independent roundings whose standard deviation the oracle reports
+#     ("sigma").  Bound: 6 sigma, plus the bf16 rounding of out (2^-8 of
+#     |out|), plus 1e-4 for fp32 accumulation order.
+#   * fp32 evaluation of the scores: 128 exact fp8 products summed in fp32, an
+#     error of a few 2^-24 of the sum of their magnitudes ("zabs" per row), so
+#     lse within 2^-16 zabs + 1e-5.
+#   * rounding decisions: the kernel rotates in fp32 arithmetic of its own and
+#     the oracle rounds the float64 rotation to fp32; where an e4m3 rounding
+#     midpoint (or a block-scale boundary) lies within their error window, both
+#     roundings are valid.  The oracle reports how far such elements can move
+#     lse and out ("lse_flip", "out_flip", zero for almost every row), and both
+#     bounds include it.
+#
+# Against the exact float64 oracle: the quality of the mode itself, on the
+# N(0, 1) workloads.  Rounding Q and K to 3-bit mantissas (relative error up to
+# 2^-4 each, standard deviation about 2^-4 / sqrt(3)) moves a logit by
+# sigma_z = c sqrt(2/3) 2^-4 |q * k|_2, about 0.05 for N(0, 1) rows.  A row
+# dominated by one key moves its lse by sigma_z: 5 sigma_z = 0.25.  Its output
+# moves by p (1 - p) sigma_z |v_a - v_b| for two competing keys, at most
+# 1/4 x 0.05 x 8 (4-sigma values of v) x 5 = 0.5; rounding V adds 2^-4 of
+# |v| on such rows.  Averaged over all outputs the error stays far smaller:
+# mean-abs 2e-2.  Wider inputs (the peaky case) are checked against the
+# quantized oracle only; their distance from exact softmax grows with the
+# logits and is reported.
+FP8_SIGMAS = 6.0
+FP8_LSE_REL = 2.0 ** -16
+FP8_LSE_ABS = 1e-5
+FP8_EXACT_OUT_MAX = 0.5
+FP8_EXACT_OUT_MEAN = 2e-2
+FP8_EXACT_LSE_MAX = 0.25
+
+
+def compare_fp8(out_gpu, lse_gpu, out_sage, lse_sage, scales, out_exact, lse_exact, label="", exact_bars=True):
+    """exact_bars: also hold the mode to its quality bar against exact softmax (N(0, 1) inputs)."""
+    sigma, zabs = scales["sigma"], scales["zabs"]
+    d = np.abs(out_gpu - out_sage)
+    bound = FP8_SIGMAS * sigma + 2.0 ** -8 * np.abs(out_sage) + 1e-4 + scales["out_flip"]
+    ld = np.abs(lse_gpu - lse_sage)
+    lbound = FP8_LSE_REL * zabs + FP8_LSE_ABS + scales["lse_flip"]
+    ex = np.abs(out_gpu - out_exact)
+    lex = np.abs(lse_gpu - lse_exact)
+    stats = dict(max_over_bound=float((d / bound).max()), rms_over_sigma=float(np.sqrt(np.mean((d / sigma) ** 2))),
+                 lse_max=float(ld.max()), lse_max_over_bound=float((ld / lbound).max()),
+                 rows_with_alternatives=int(np.count_nonzero(scales["lse_flip"])),
+                 exact_out_max=float(ex.max()), exact_out_mean=float(ex.mean()), exact_lse_max=float(lex.max()))
+    say(f"{label} fp8: vs quantized oracle: max err/bound {stats['max_over_bound']:.3f}, rms err/sigma "
+        f"{stats['rms_over_sigma']:.3f}, lse max {stats['lse_max']:.2e} (max err/bound {stats['lse_max_over_bound']:.3f}, "
+        f"rows with alternative roundings {stats['rows_with_alternatives']}); "
+        f"vs exact: out max {stats['exact_out_max']:.3e} mean {stats['exact_out_mean']:.3e} lse max "
+        f"{stats['exact_lse_max']:.3e}")
+    assert np.all(np.isfinite(out_gpu)) and np.all(np.isfinite(lse_gpu))
+    assert stats["max_over_bound"] <= 1.0, (label, stats, np.unravel_index((d / bound).argmax(), d.shape))
+    assert stats["lse_max_over_bound"] <= 1.0, (label, stats, np.unravel_index((ld / lbound).argmax(), ld.shape))
+    if exact_bars:
+        assert stats["exact_out_max"] <= FP8_EXACT_OUT_MAX, (label, stats)
+        assert stats["exact_out_mean"] <= FP8_EXACT_OUT_MEAN, (label, stats)
+        assert stats["exact_lse_max"] <= FP8_EXACT_LSE_MAX, (label, stats)
+    return stats

@@ -123,10 +123,12 @@ def _cfg(theta=10000.0, dims=(32, 48, 48)):
 
 
 def _fwd(L, q=FAKE, k=FAKE * 2, v=FAKE * 3, cu=FAKE * 4, pos=FAKE * 5, out=1 << 40, lse=1 << 41, N=64, Hh=2,
-         Dh=128, ns=1, ms=64, scale=0.0, cfg=None, ws=1 << 42, wsb=None):
+         Dh=128, ns=1, ms=64, scale=0.0, cfg=None, ws=1 << 42, wsb=None, fp8=False):
+    size = L.h3attn_varlen_fwd_fp8_workspace_size if fp8 else L.h3attn_varlen_fwd_workspace_size
+    fwd = L.h3attn_varlen_fwd_fp8 if fp8 else L.h3attn_varlen_fwd
     if wsb is None:
-        wsb = L.h3attn_varlen_fwd_workspace_size(N, Hh, 128, ns)
-    return L.h3attn_varlen_fwd(q, k, v, cu, pos, out, lse, N, Hh, Dh, ns, ms, scale, cfg or _cfg(), ws, wsb, None)
+        wsb = size(N, Hh, 128, ns)
+    return fwd(q, k, v, cu, pos, out, lse, N, Hh, Dh, ns, ms, scale, cfg or _cfg(), ws, wsb, None)
 
 
 @pytest.mark.parametrize(
@@ -153,8 +155,9 @@ def _fwd(L, q=FAKE, k=FAKE * 2, v=FAKE * 3, cu=FAKE * 4, pos=FAKE * 5, out=1 << 
         (dict(lse=(1 << 40) + 64), H.H3ATTN_ERR_INVALID_ARG),  # lse overlaps out
     ],
 )
-def test_varlen_fwd_argument_checks(L, kw, status):
-    assert _fwd(L, **kw) == status
+@pytest.mark.parametrize("fp8", [False, True])
+def test_varlen_fwd_argument_checks(L, kw, status, fp8):
+    assert _fwd(L, fp8=fp8, **kw) == status
     assert H.h3attn_last_error() != ""
 
 
@@ -169,6 +172,7 @@ def test_varlen_fwd_argument_checks(L, kw, status):
 )
 def test_rope_config_checks(L, dims, theta, status):
     assert _fwd(L, cfg=_cfg(theta, dims)) == status
+    assert _fwd(L, cfg=_cfg(theta, dims), fp8=True) == status
     assert L.h3attn_rope_apply(FAKE, FAKE, FAKE * 2, 8, 1, 128, _cfg(theta, dims), None) == status
 
 
@@ -180,6 +184,7 @@ def test_null_rope_config(L):
 def test_zero_tokens_is_a_noop(L):
     # N = 0 returns OK without touching any pointer or launching anything
     assert _fwd(L, q=0, k=0, v=0, cu=0, pos=0, out=0, lse=0, N=0, ms=0, ws=0, wsb=0) == H.H3ATTN_OK
+    assert _fwd(L, q=0, k=0, v=0, cu=0, pos=0, out=0, lse=0, N=0, ms=0, ws=0, wsb=0, fp8=True) == H.H3ATTN_OK
     assert L.h3attn_rope_apply(None, None, None, 0, 1, 128, _cfg(), None) == H.H3ATTN_OK
 
 
@@ -197,3 +202,25 @@ def test_workspace_size_formula(L):
         rows = 64 * ((N + 63) // 64 + ns)
         assert L.h3attn_varlen_fwd_workspace_size(N, Hh, 128, ns) == 2 * Hh * rows * 128 * 2 + Hh * (rows // 64) * 4
     assert L.h3attn_varlen_fwd_workspace_size(10, 1, 64, 1) == 0
+
+
+def test_fp8_workspace_size_formula(L):
+    # per head: 64 * (ceil(N / 64) + n_seqs) rows of 128 bytes for keys and for values, then two
+    # arrays of one 32-bit word per 64-row tile (key scales, value scales), each padded to 256 bytes
+    for N, Hh, ns in [(1, 1, 1), (64, 2, 1), (65, 3, 4), (130048, 5, 1), (45760, 16, 4)]:
+        rows = 64 * ((N + 63) // 64 + ns)
+        scales = (Hh * (rows // 64) * 4 + 255) // 256 * 256
+        assert L.h3attn_varlen_fwd_fp8_workspace_size(N, Hh, 128, ns) == 2 * Hh * rows * 128 + 2 * scales
+    assert L.h3attn_varlen_fwd_fp8_workspace_size(10, 1, 64, 1) == 0
+
+
+def test_fp8_stage_argument_checks(L):
+    wsb = L.h3attn_varlen_fwd_fp8_workspace_size(64, 2, 128, 1)
+    assert L.h3attn_varlen_kv_prologue_fp8(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, 64, 2, 128, 1, 64, _cfg(), 1 << 42,
+                                           wsb - 1, None) == H.H3ATTN_ERR_WORKSPACE
+    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, 1 << 40, 1 << 41, 64, 2, 128, 1, 64, 0.0, _cfg(),
+                                         1 << 42, wsb - 1, None) == H.H3ATTN_ERR_WORKSPACE
+    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, FAKE, 1 << 41, 64, 2, 128, 1, 64, 0.0, _cfg(),
+                                         1 << 42, wsb, None) == H.H3ATTN_ERR_INVALID_ARG   # out overlaps q
+    assert L.h3attn_varlen_kv_prologue_fp8(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, 64, 2, 64, 1, 64, _cfg(), 1 << 42,
+                                           wsb, None) == H.H3ATTN_ERR_UNSUPPORTED

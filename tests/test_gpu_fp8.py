@@ -1,0 +1,157 @@
+"""GPU parity of the lossy FP8 mode (h3attn_varlen_fwd_fp8) through the C ABI.
+
+Bars (tests/helpers.py, compare_fp8): against the block-quantized float64
+oracle (oracle.sage, P unrounded) every output element within 6 standard
+deviations of the P rounding the oracle predicts, plus the bf16 rounding of
+out; lse within fp32 score evaluation error (2^-16 of the row's largest sum
+of absolute products); both plus what the oracle reports alternative
+roundings next to an e4m3 midpoint can change; against
+the exact float64 oracle the mode's own quality bar on N(0, 1) inputs (out
+max-abs 0.5, mean-abs 2e-2, lse max-abs 0.25).  Small cases are compared in full,
+the workloads on sampled rows in the launch configuration the bench times.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import Case, bf16_bits, compare_fp8, device_to_f64, ragged_segments, say
+from joint_sequence_attention_amd import h3attn as H
+from joint_sequence_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(c, label, exact_bars=True, scale=None, **kw):
+    out, lse = c.run_fp8(softmax_scale=scale or 0.0, **kw)
+    o_s, l_s, es = c.sage_rows(scale=scale, **kw)
+    o_e, l_e = c.oracle_full(scale=scale, **kw)
+    return compare_fp8(device_to_f64(out), device_to_f64(lse), o_s, l_s, es, o_e, l_e, label=label,
+                       exact_bars=exact_bars)
+
+
+@pytest.mark.parametrize("seed", [1, 1001])
+def test_fp8_tiny_full(gpu, seed):
+    cfg = wl.config("tiny")
+    c = Case(cfg["segments"], cfg["heads"], seed)
+    say(f"fp8 tiny seed {seed}: N={c.N} H={c.heads}")
+    _full(c, f"tiny/{seed}")
+
+
+@pytest.mark.parametrize("heads", [1, 3])
+def test_fp8_ragged_segments_full(gpu, heads):
+    c = Case(ragged_segments(), heads, 140 + heads)
+    say(f"fp8 ragged: lens={c.lens.tolist()} H={heads}")
+    _full(c, "ragged")
+
+
+def test_fp8_peaky_softmax_full(gpu):
+    # q x 4: logits four times wider; checked against the quantized oracle (the
+    # distance from exact softmax grows with the logits and is only reported).
+    c = Case(ragged_segments(), 2, 150, qscale=4.0)
+    say(f"fp8 peaky: lens={c.lens.tolist()}")
+    _full(c, "peaky", exact_bars=False)
+
+
+@pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va"])
+@pytest.mark.parametrize("seed_offset", [0, wl.ROBUSTNESS_SEED_OFFSET])
+def test_fp8_workload_sampled_rows(gpu, name, seed_offset):
+    cfg = wl.config(name)
+    seed = cfg["seed"] + seed_offset
+    c = Case(cfg["segments"], cfg["heads"], seed)
+    say(f"fp8 {name} seed {seed}: N={c.N} H={c.heads} segments={len(c.lens)}")
+    out, lse = c.run_fp8()
+    out64, lse64 = device_to_f64(out), device_to_f64(lse)
+    assert np.all(np.isfinite(out64)) and np.all(np.isfinite(lse64))
+    rows = c.sample_rows(n_random=64 if c.N > 100000 else 128, seed=seed)
+    o_s, l_s, es = c.sage_rows(rows)
+    o_e, l_e = c.oracle_rows(rows)
+    compare_fp8(out64[rows], lse64[:, rows], o_s, l_s, es, o_e, l_e, label=f"{name}/{seed} ({len(rows)} rows)")
+
+
+def test_fp8_explicit_scale_and_rope_config(gpu):
+    c = Case(ragged_segments(), 2, 164)
+    say("fp8 explicit scale / rope config")
+    _full(c, "scale/theta", scale=0.05, theta=500.0, dims=(64, 32, 32))
+
+
+def test_fp8_two_stages_equal_fused_call_and_deterministic(gpu):
+    import torch
+    c = Case(ragged_segments(), 3, 161)
+    out, lse = c.run_fp8()
+    ws = H.alloc_workspace(c.N, 3, len(c.lens), fp8=True)
+    H.h3attn_varlen_kv_prologue_fp8(c.k, c.v, c.cu_d, c.pos_d, c.max_seqlen, ws)
+    out2, lse2 = H.h3attn_varlen_attention_fp8(c.q, c.cu_d, c.pos_d, c.max_seqlen, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(out), bf16_bits(out2))
+    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+    out3, lse3 = c.run_fp8()
+    assert np.array_equal(bf16_bits(out), bf16_bits(out3))
+    assert np.array_equal(lse.cpu().numpy(), lse3.cpu().numpy())
+
+
+def test_fp8_segment_isolation_bitwise(gpu):
+    import torch
+    segs = [[wl.visual(T, 6, 10), wl.audio(32 * T // 4, T, attached=True)] for T in (3, 5, 2)]
+    c = Case(segs, 2, 163)
+    out, lse = c.run_fp8()
+    for s in range(len(segs)):
+        a, b = int(c.cu[s]), int(c.cu[s + 1])
+        cu1 = torch.tensor([0, b - a], dtype=torch.int32, device="cuda")
+        o1, l1 = H.h3attn_varlen_fwd_fp8(c.q[a:b].contiguous(), c.k[a:b].contiguous(), c.v[a:b].contiguous(), cu1,
+                                         c.pos_d[a:b].contiguous(), b - a)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(out[a:b]), bf16_bits(o1))
+        assert np.array_equal(lse[:, a:b].cpu().numpy(), l1.cpu().numpy())
+
+
+def test_fp8_length_one_and_empty_segments(gpu):
+    import torch
+    segs = [[], [wl.visual(1, 1, 1)], [], [wl.audio(1, 1.0, attached=False)], [wl.visual(1, 5, 7)], []]
+    c = Case(segs, 2, 166)
+    out, lse = H.h3attn_varlen_fwd_fp8(c.q, c.k, c.v, c.cu_d, c.pos_d, c.N)  # generous max_seqlen
+    torch.cuda.synchronize()
+    o_s, l_s, es = c.sage_rows()
+    o_e, l_e = c.oracle_full()
+    compare_fp8(device_to_f64(out), device_to_f64(lse), o_s, l_s, es, o_e, l_e, label="length-1/empty")
+
+
+def test_fp8_zero_tokens_noop(gpu):
+    import torch
+    q = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(2, dtype=torch.int32, device="cuda")
+    pos = torch.empty((0, 3), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out, lse = H.h3attn_varlen_fwd_fp8(q, q, q, cu, pos, 0, workspace=ws)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 128) and lse.shape == (2, 0)
+
+
+# ---- limits of the launch shape --------------------------------------------------------------
+
+
+def test_fp8_long_single_segment_sampled_rows(gpu):
+    segs = [[wl.visual(64, 64, 64)]]
+    c = Case(segs, 1, seed=171)
+    say(f"fp8 long segment: N={c.N} H=1")
+    out, lse = c.run_fp8()
+    out64, lse64 = device_to_f64(out), device_to_f64(lse)
+    assert np.all(np.isfinite(out64)) and np.all(np.isfinite(lse64))
+    rows = c.sample_rows(n_random=24, seed=171)
+    o_s, l_s, es = c.sage_rows(rows)
+    o_e, l_e = c.oracle_rows(rows)
+    compare_fp8(out64[rows], lse64[:, rows], o_s, l_s, es, o_e, l_e, label=f"long segment ({len(rows)} rows)")
+
+
+def test_fp8_two_thousand_short_segments_full(gpu):
+    rng = np.random.default_rng(172)
+    lengths = rng.integers(0, 65, size=2000)
+    segs = [[wl.visual(1, 1, int(n))] if n else [] for n in lengths]
+    c = Case(segs, 2, seed=172)
+    say(f"fp8 2000 segments: N={c.N} H=2, empty={int((lengths == 0).sum())}")
+    _full(c, "2000 segments")
+
+
+def test_fp8_many_heads_full(gpu):
+    c = Case([[wl.visual(2, 16, 16)]], 128, seed=173)
+    say(f"fp8 128 heads: N={c.N} H=128")
+    _full(c, "128 heads")

@@ -146,6 +146,16 @@ def test_sage_p_rounding_stays_within_its_bound():
     bound = (err_p @ np.abs(v[:, 0])) / p.sum(axis=1, keepdims=True)
     assert np.all(np.abs(out_p[:, 0] - out_u[:, 0]) <= bound * (1 + 1e-12))
     assert np.max(np.abs(out_p - out_u)) > 0           # P rounding is really applied
+    # the reported spread: the same per-probability bound, squared over 3, summed with v^2
+    _, _, es = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, error_scales=True)
+    sig = es["sigma"]
+    want = np.sqrt((err_p ** 2 @ v[:, 0] ** 2) / 3.0) / p.sum(axis=1, keepdims=True)
+    assert np.allclose(sig[:, 0], want, rtol=1e-12, atol=0)
+    zabs = np.array([max(sum(abs(q[i, 0, d] * k[j, 0, d]) for d in range(D)) for j in range(n)) for i in range(0, n, 37)])
+    assert np.allclose(es["zabs"][0, ::37], zabs / math.sqrt(D), rtol=1e-12, atol=0)
+    # and the actual rounding error, across all rows and dims, is of that size
+    ratio = np.abs(out_p - out_u) / sig
+    assert np.sqrt(np.mean(ratio ** 2)) < 1.0 and ratio.max() < 6.0
 
 
 def _brute_sage(q, k, v, cu, scale):
@@ -242,3 +252,53 @@ def test_sage_close_to_exact_on_the_tiny_workload():
     assert np.max(np.abs(lse_s - lse_e)) < 0.05
     assert np.max(np.abs(out_s - out_e)) < 0.1
     assert np.mean(np.abs(out_s - out_e)) < 0.01
+
+
+def test_rotation_error_bound_covers_float32_rotation():
+    # An independent float32 evaluation of the rotation (numpy float32 arithmetic, angles
+    # rounded to float32 first) stays within the bound the oracle states for fp32 kernels.
+    from oracle.rope import rope_frequencies
+    rng = np.random.default_rng(12)
+    n, h = 300, 2
+    x = rng.standard_normal((n, h, D)).astype(np.float32).astype(np.float64)
+    pos = np.stack([rng.integers(0, 300, n), rng.integers(0, 48, n), rng.integers(0, 84, n)], axis=1).astype(float)
+    exact = oracle.rope(x, pos)
+    y = np.empty_like(exact)
+    off = 0
+    for axis, width in enumerate((32, 48, 48)):
+        om = rope_frequencies(10000.0, width).astype(np.float32)
+        phi = pos[:, axis].astype(np.float32)[:, None] * om[None, :]
+        c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]
+        x0 = x[:, :, off:off + width:2].astype(np.float32)
+        x1 = x[:, :, off + 1:off + width:2].astype(np.float32)
+        y[:, :, off:off + width:2] = x0 * c - x1 * s
+        y[:, :, off + 1:off + width:2] = x0 * s + x1 * c
+        off += width
+    assert np.all(np.abs(y - exact) <= sage.rotation_error_bound(x, pos))
+
+
+def test_quantize_block_margin():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((16, D))
+    w = np.full_like(x, 1e-3)
+    q, change = sage.quantize_block_margin(x, w)
+    assert np.array_equal(q, sage.quantize_block(x))
+    # a value whose window holds no midpoint rounds the same way anywhere inside it
+    for _ in range(20):
+        xp = x + rng.uniform(-1, 1, x.shape) * w
+        qp = sage.quantize_block(xp)
+        if int(sage.pow2_scale_exponent(np.abs(xp).max())) != int(sage.pow2_scale_exponent(np.abs(x).max())):
+            continue
+        moved = qp != q
+        assert np.all(change[moved] > 0)
+        assert np.all(np.abs(qp - q)[moved] <= change[moved])
+    # an exact midpoint is flagged with one step (1.0625 sits between 1.0 and 1.125 at scale 2^0)
+    blk = np.zeros(4)
+    blk[0] = 416.0                            # scale 2^0, clear of the boundary at 448
+    blk[1] = 1.0625
+    q, change = sage.quantize_block_margin(blk, np.full(4, 1e-9))
+    assert change[1] == 0.125 and change[0] == 0 and change[2] == 0
+    # a block maximum next to a scale boundary flags the whole block
+    blk[0] = 448.0 * (1 + 1e-12)
+    q, change = sage.quantize_block_margin(blk, np.full(4, 1e-6))
+    assert np.all(change > 0)
