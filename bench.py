@@ -12,6 +12,9 @@ time.  roofline: the attention kernel alone, timed with HIP events recorded on
 the stream it is launched on, against the bf16 dense MFMA peak.
 cpu_baseline: the float64 oracle on a bounded sample of query rows of the same
 workload, on this host's cores.
+fp8_mode: the same step through the lossy FP8 entry points (h3attn_varlen_fwd_fp8:
+e4m3 Q/K/P/V with block scales), with its own roofline against the fp8 dense
+MFMA peak.  It is reported beside the bf16 metric, never in its place.
 """
 
 from __future__ import annotations
@@ -27,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 
 # HBM bytes of one attn_fwd_kernel launch on the 1344x768 workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
@@ -148,11 +152,19 @@ def survey_workload(name, steps, warmup):
     attn_ms = timed(lambda: H.h3attn_varlen_attention(q, cu_d, pos_d, max_seqlen, ws, out=out, lse=lse))
     rope_ms = timed(lambda: H.h3attn_rope_apply(q, pos_d, out=y))
     rope_bytes = 2 * N * heads * 128 * 2 + N * 12
+    ws8 = H.alloc_workspace(N, heads, len(lens), dev, fp8=True)
+    fp8_step_ms = timed(lambda: H.h3attn_varlen_fwd_fp8(q, k, v, cu_d, pos_d, max_seqlen, out=out, lse=lse,
+                                                         workspace=ws8))
+    H.h3attn_varlen_kv_prologue_fp8(k, v, cu_d, pos_d, max_seqlen, ws8)
+    fp8_attn_ms = timed(lambda: H.h3attn_varlen_attention_fp8(q, cu_d, pos_d, max_seqlen, ws8, out=out, lse=lse))
     return {"workload": name, "tokens": N, "heads": heads, "segments": int(len(lens)), "flop": flop,
             "step_ms": round(step_ms, 4), "step_tflops": round(flop / step_ms / 1e9, 1),
             "attn_ms": round(attn_ms, 4), "attn_tflops": round(flop / attn_ms / 1e9, 1),
             "attn_pct_of_peak": round(100 * flop / attn_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "rope_apply_ms": round(rope_ms, 4), "rope_apply_gbps": round(rope_bytes / rope_ms / 1e6, 1)}
+            "rope_apply_ms": round(rope_ms, 4), "rope_apply_gbps": round(rope_bytes / rope_ms / 1e6, 1),
+            "fp8_step_ms": round(fp8_step_ms, 4), "fp8_attn_ms": round(fp8_attn_ms, 4),
+            "fp8_attn_tflops": round(flop / fp8_attn_ms / 1e9, 1),
+            "fp8_attn_pct_of_fp8_peak": round(100 * flop / fp8_attn_ms / 1e9 / PEAK_FP8_TFLOPS, 2)}
 
 
 def main():
@@ -252,6 +264,43 @@ def main():
     print(f"[bench] {ms_per_step:.3f} ms/step, attention kernel {attn_ms:.3f} ms -> {achieved:.1f} TFLOP/s "
           f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of peak)", file=sys.stderr, flush=True)
 
+    # The lossy FP8 mode on the same resident inputs: prologue + attention per step, the attention
+    # kernel timed by events on its stream.
+    ws8 = H.alloc_workspace(N, heads, len(lens), dev, fp8=True)
+
+    def step8(ev_a=None, ev_b=None):
+        H.h3attn_varlen_kv_prologue_fp8(k, v, cu_d, pos_d, max_seqlen, ws8)
+        if ev_a is not None:
+            ev_a.record()
+        H.h3attn_varlen_attention_fp8(q, cu_d, pos_d, max_seqlen, ws8, out=out, lse=lse)
+        if ev_b is not None:
+            ev_b.record()
+
+    for _ in range(args.warmup):
+        step8()
+    torch.cuda.synchronize()
+    evs8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start.record()
+    for i in range(args.steps):
+        step8(*evs8[i])
+    stop.record()
+    torch.cuda.synchronize()
+    fp8_ms_per_step = start.elapsed_time(stop) / args.steps
+    fp8_attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs8]))
+    fp8_achieved = flop / (fp8_attn_ms * 1e-3) / 1e12
+    if not (torch.isfinite(out.float()).all() and torch.isfinite(lse).all()):
+        print("[bench] non-finite fp8 output", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] fp8 mode: {fp8_ms_per_step:.3f} ms/step, attention kernel {fp8_attn_ms:.3f} ms -> "
+          f"{fp8_achieved:.1f} TFLOP/s ({100 * fp8_achieved / PEAK_FP8_TFLOPS:.1f}% of fp8 peak)", file=sys.stderr,
+          flush=True)
+    fp8 = {"mode": "lossy FP8 (SAGE-style e4m3 Q/K/P/V, block scales), h3attn_varlen_fwd_fp8",
+           "value": round(flop / (fp8_ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(fp8_ms_per_step, 4), "dtype": "fp8 e4m3 operands, fp32 accumulate",
+           "roofline": {"bound": "mfma", "achieved": round(fp8_achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(fp8_achieved / PEAK_FP8_TFLOPS, 4),
+                        "kernel": "attn_fwd_fp8_kernel", "kernel_ms": round(fp8_attn_ms, 4)}}
+
     cpu = None
     if not args.no_cpu_baseline:
         c = {"qb": qb, "kb": kb, "vb": vb, "cu": cu, "pos": pos, "N": N, "heads": heads}
@@ -280,6 +329,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counted_traffic(name),
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
+        "fp8_mode": fp8,
     }
     print(json.dumps(rec), flush=True)
 

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) koff[ks][hf] = k8_lds_offset(l32, 4 * ks + 2 * g + hf);
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) voff[hf] = v8_lds_offset(l32, 2 * g + hf);
+  for (int hf = 0; hf < 2; ++hf) voff[hf] = F8_VBASE + v8_lds_offset(l32, 2 * g + hf);
   // The 16-key block of the keys this lane feeds, per subtile: 2u + (l32 >= 16).
   const unsigned ksh0 = l32 >= 16 ? 8u : 0u, ksh1 = ksh0 + 16u;
 
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   };
   auto vfrag = [&](auto SLOT, int db) __attribute__((always_inline)) {
     const int slot = int(SLOT);
-    const char* base = smem + F8_VBASE + slot * F8_TILE_BYTES + db * 2048;
+    const char* base = smem + slot * F8_TILE_BYTES + db * 2048;  // voff holds the value ring's base
     const u32x4 a = *reinterpret_cast<const u32x4*>(base + voff[0]);
     const u32x4 b = *reinterpret_cast<const u32x4*>(base + voff[1]);
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -419,26 +419,27 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     }
   };
   auto pack_unit = [&](int j, const float (&p)[4], i32x8& pw, float& rs) __attribute__((always_inline)) {
-    unsigned w = pack_e4m3x4(p[0], p[1], p[2], p[3]);
-    float r = (j & 3) == 0 ? (p[0] + p[1]) + (p[2] + p[3]) : rs + ((p[0] + p[1]) + (p[2] + p[3]));
+    // both halves of the word are written, so its previous contents may seed the conversion
+    unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], unsigned(pw[j]), false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+    float r = j == 0 ? (p[0] + p[1]) + (p[2] + p[3]) : rs + ((p[0] + p[1]) + (p[2] + p[3]));
     pin(w);
     pin(r);
     pw[j] = int(w);
     rs = r;
   };
-  // After the exponentials of subtile U of tile t (buffer B): the rare path
-  // that moves the running maximum, then the row sum.  The rare path rescales
-  // O and l and recomputes the subtile's probabilities; on subtile 1 it also
-  // rescales the subtile-0 bytes already formed with the old maximum (one
-  // more e4m3 rounding of those values, on this rare path only).
-  auto settle = [&](auto B, auto U, i32x8& pw, float rs) __attribute__((always_inline)) {
+  // After the exponentials of tile t (buffer B): the rare path that moves the
+  // running maximum (rescaling O and l and recomputing the tile's
+  // probabilities), then the row sum.
+  auto settle = [&](auto B, i32x8& pw, float rs) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
-    constexpr int u = decltype(U)::value;
     const bool over = !(rs <= LAZY_SUM);  // also true for inf and NaN
     if (__builtin_amdgcn_ballot_w64(over) != 0) {
-      float mx = sc[b][u][0];
+      float mx = sc[b][0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
       const float tmax = pair_max(mx) * cq;
       const float m_new = fmaxf(mm, tmax - P_SHIFT);
       const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf
@@ -448,21 +449,12 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= a;
-      if (u == 1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pw[j], false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pw[j], true);
-          pw[j] = int(pack_e4m3x4(lo[0] * a, lo[1] * a, hi[0] * a, hi[1] * a));
-        }
-      }
       rs = 0.0f;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * u + jj;
+      for (int j = 0; j < 8; ++j) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][u][4 * jj + i], cq, -mm));
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cq, -mm));
         pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
         rs += (p[0] + p[1]) + (p[2] + p[3]);
       }
@@ -485,6 +477,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     constexpr bool do_qk = decltype(QK)::value != 0;
     constexpr bool do_pv = decltype(PV)::value != 0;
     i32x8 fr[2], pw;
+    asm volatile("" : "=v"(pw));  // every word is written below; no need to clear it first
     float rs = 0.0f;
     if (do_pv) {
       fr[0] = vfrag(vslot, 0);
@@ -506,8 +499,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       pack_unit(j, p, pw, rs);
       __builtin_amdgcn_sched_barrier(0);
     }
-    settle(ic<b>(), ic<0>(), pw, rs);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 4; j < 8; ++j) {
       if (do_qk) {
@@ -527,7 +518,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       pack_unit(j, p, pw, rs);
       __builtin_amdgcn_sched_barrier(0);
     }
-    settle(ic<b>(), ic<1>(), pw, rs);
+    settle(ic<b>(), pw, rs);
     pf[b] = pw;
   };
 
@@ -558,6 +549,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     region(ic<b>(), ic<0>(), ic<1>(), 0, (last_t - 1) & 7, kq0, kq1, vq);
     const unsigned vl = vscale(last_t);
     ring_barrier<0>();  // V(t) has landed
+    __builtin_amdgcn_sched_barrier(0);
     pv_alone(ic<b>(), last_t & 7, vl);
   };
   {
