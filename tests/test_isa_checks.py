@@ -10,6 +10,10 @@ without a GPU:
 * If a v_dot2 chain appears, no accumulator is fed the same source register
   twice in a row: this toolchain miscompiles a dot2 whose source is an element
   of a 128-bit vector (it reads element 0 every time).
+* The FP8 mode runs both contractions on v_mfma_scale_f32_32x32x64_f8f6f4, has
+  no packed-fp32 instructions, and its main loop neither spills nor copies
+  register blocks (the few spills the compiler leaves sit in the once-per-
+  workgroup last iteration).
 """
 
 import os
@@ -23,15 +27,24 @@ from joint_sequence_attention_amd import build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.fixture(scope="module")
-def isa(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "attn.s"
+def _compile(tmp_path_factory, source):
+    out = tmp_path_factory.mktemp("isa") / (source + ".s")
     cmd = [build.hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", build.CSRC, "-S", "--cuda-device-only",
-           os.path.join(build.CSRC, "attn_kernels.hip"), "-o", str(out)]
+           os.path.join(build.CSRC, source), "-o", str(out)]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     assert proc.returncode == 0, proc.stderr
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def isa(tmp_path_factory):
+    return _compile(tmp_path_factory, "attn_kernels.hip")
+
+
+@pytest.fixture(scope="module")
+def isa_fp8(tmp_path_factory):
+    return _compile(tmp_path_factory, "attn_fp8.hip")
 
 
 def test_mfma_instructions(isa):
@@ -51,3 +64,42 @@ def test_no_spills_and_no_packed_fp32(isa):
     scratch = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", isa)
     assert scratch and all(int(c) == 0 for c in scratch)
     assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", isa)
+
+
+def _loop_blocks(isa_text, kernel_substring):
+    """Basic blocks of the kernel's loop body (the compiler marks them 'in Loop' / 'Loop Header')."""
+    start = isa_text.index(kernel_substring)
+    end = isa_text.index(".Lfunc_end", start)
+    blocks, cur, in_loop = [], [], False
+    for ln in isa_text[start:end].split("\n"):
+        if ln.startswith(".LBB") or ln.startswith("; %bb"):
+            if in_loop:
+                blocks.append(cur)
+            cur, in_loop = [], ("Loop" in ln)
+        cur.append(ln)
+    if in_loop:
+        blocks.append(cur)
+    return blocks
+
+
+def test_fp8_mfma_and_no_packed_fp32(isa_fp8):
+    assert "v_mfma_scale_f32_32x32x64_f8f6f4" in isa_fp8
+    assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", isa_fp8)
+
+
+def test_fp8_main_loop_has_no_spills_or_block_copies(isa_fp8):
+    blocks = _loop_blocks(isa_fp8, "attn_fwd_fp8_kernel")
+    assert len(blocks) >= 8
+    for bl in blocks:
+        text = "\n".join(bl)
+        assert "scratch_" not in text
+        # a run of register moves would be the register allocator copying an accumulator (or the
+        # output block) from one set of registers to another on every iteration
+        run = longest = 0
+        for ln in bl:
+            if re.match(r"\s+v_mov_b(32|64)_e32\s+v", ln):
+                run += 1
+                longest = max(longest, run)
+            elif ln.strip() and not ln.strip().startswith(";"):
+                run = 0
+        assert longest < 8, text[:400]
