@@ -36,6 +36,23 @@ The steps, in that order, with the readings taken where the page is silent:
    to a running maximum instead, so its P rounding differs element by element;
    both are draws of the same rounding noise, which the GPU tests bound.
 
+Skip-Softmax (optional, ``skip_threshold``).  The same recipe section offers
+a second lossy option, Skip-Softmax sparse attention with a direct threshold
+(0.05 there): tiles of keys whose probabilities are all below the threshold,
+relative to the running maximum, are left out.  The page names the knob, not
+the rule; the reading taken here, stated so that the result is a function of
+the logits alone:
+
+* queries go in blocks of 32 rows and keys in tiles of 64 (the FP8 kernel's
+  units), both counted from the segment start, tiles in key order;
+* for each row, the running maximum before tile T is the largest logit of
+  the tiles before T (minus infinity for the first tile), whether or not
+  they were skipped;
+* tile T is skipped for a block when every valid row r of the block has
+  max_{j in T} z_rj < running_max_r + ln(threshold);
+* a skipped tile contributes nothing to that block's softmax: out and lse
+  are exact softmax over the keys of the tiles that are kept.
+
 Rounding decisions near a midpoint.  A kernel rotates in its own fp32
 arithmetic, within 2^-22 (1 + |phi|)(|x0| + |x1|) of the exact rotation
 (angle rounding, sin/cos and the multiply-adds); this oracle's float32 values
@@ -61,6 +78,8 @@ Q_BLOCK = 1                        # query rows per scale
 K_BLOCK = 16                       # keys per scale
 V_BLOCK = 64                       # keys per scale (all dims)
 P_SCALE_LOG2 = 4                   # P is quantized as p * 2**4
+SKIP_QUERY_BLOCK = 32              # Skip-Softmax: query rows that decide together
+SKIP_KEY_TILE = 64                 # Skip-Softmax: keys skipped together
 
 
 def round_e4m3(x) -> np.ndarray:
@@ -183,10 +202,17 @@ def _quantized_segment_kv(kr_seg, kw_seg, v_seg):
     return kq, kc, vq
 
 
-def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None):
+def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None, keep=None, amb=None, tile=64):
+    """One head of one segment for a set of query rows.
+
+    keep: bool [R, S], the keys that count (all when None).  amb: bool [R, n_tiles], tiles whose
+    skip decision could go either way for the row's block (their effect is added to the error
+    scales).
+    """
     z = (q8 @ k8.T) * scale
-    m = z.max(axis=1, keepdims=True)
-    p = np.exp(z - m)
+    zk = z if keep is None else np.where(keep, z, -np.inf)
+    m = zk.max(axis=1, keepdims=True)
+    p = np.exp(zk - m)
     l = p.sum(axis=1, keepdims=True)
     pw = np.ldexp(round_e4m3(np.ldexp(p, P_SCALE_LOG2)), -P_SCALE_LOG2) if quantize_p else p
     out = (pw @ v8) / l
@@ -194,7 +220,7 @@ def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None):
     # Spread of the P rounding: each probability moves by at most half an e4m3 ulp, 2^-4 of
     # itself, or half the subnormal step, 2^-14 in these units; a rounding error spread evenly
     # over that interval has standard deviation (bound) / sqrt(3).
-    e = np.maximum(p * 2.0 ** -4, 2.0 ** -(10 + P_SCALE_LOG2))
+    e = np.where(p > 0, np.maximum(p * 2.0 ** -4, 2.0 ** -(10 + P_SCALE_LOG2)), 0.0)
     sigma = np.sqrt(((e * e) @ (v8 * v8)) / 3.0) / l
     # Largest sum of absolute products behind one logit of the row: the scale of
     # the rounding error any finite-precision evaluation of the row's scores has.
@@ -212,11 +238,55 @@ def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None):
     av = np.abs(v8)
     ao = np.abs(out)
     out_flip = (pd @ av + pd.sum(axis=1, keepdims=True) * ao + lse_flip[:, None] * (p @ av + l * ao)) / l
-    return out, lse, (sigma, zabs, 1.25 * lse_flip, 1.25 * out_flip)
+    lse_flip = 1.25 * lse_flip
+    out_flip = 1.25 * out_flip
+    if amb is not None and amb.any():
+        # A tile whose decision could go the other way: with weight w = (sum of its probabilities
+        # relative to this row's maximum) / l, keeping or dropping it moves lse by at most
+        # w / (1 - w) and out by that times (max |v| over the tile + |out|).
+        pall = np.exp(z - m)
+        S = k8.shape[0]
+        for t in np.nonzero(amb.any(axis=0))[0]:
+            rows_t = amb[:, t]
+            j0, j1 = t * tile, min(S, (t + 1) * tile)
+            w = pall[rows_t, j0:j1].sum(axis=1) / l[rows_t, 0]
+            wb = w / np.maximum(1.0 - w, 1e-3)
+            vmax = np.abs(v8[j0:j1]).max(axis=0)
+            lse_flip[rows_t] += wb
+            out_flip[rows_t] += wb[:, None] * (vmax[None, :] + ao[rows_t])
+    return out, lse, (sigma, zabs, lse_flip, out_flip)
+
+
+def skip_decisions(z, valid, threshold, tile=64, delta=None):
+    """Skip-Softmax decisions for one query block.
+
+    z: float64 [R, S] logits of the block's rows (natural units); valid: bool [R], the rows that
+    exist.  Returns (skip bool [n_tiles], ambiguous bool [n_tiles]).  A decision is ambiguous
+    when moving each row's logits by up to delta [R] (its evaluation error) could change it.
+    """
+    R, S = z.shape
+    n_tiles = (S + tile - 1) // tile
+    skip = np.zeros(n_tiles, dtype=bool)
+    amb = np.zeros(n_tiles, dtype=bool)
+    if not threshold or threshold <= 0 or not valid.any():
+        return skip, amb
+    ln_thr = math.log(threshold)
+    zv = z[valid]
+    d = np.zeros(zv.shape[0]) if delta is None else np.asarray(delta)[valid]
+    running = np.full(zv.shape[0], -np.inf)
+    for t in range(n_tiles):
+        tm = zv[:, t * tile:min(S, (t + 1) * tile)].max(axis=1)
+        margin = running + ln_thr - tm           # > 0: this row lets the tile go
+        skip[t] = bool(np.all(margin > 0))
+        could_skip = bool(np.all(margin > -2 * d))
+        could_keep = bool(np.any(margin < 2 * d))
+        amb[t] = could_skip and could_keep
+        running = np.maximum(running, tm)
+    return skip, amb
 
 
 def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, theta=10000.0, dims=(32, 48, 48),
-                        scale=None, quantize_p=True, error_scales=False):
+                        scale=None, quantize_p=True, error_scales=False, skip_threshold=None):
     """Block-quantized FP8 attention for selected query rows (all rows when ``rows`` is None).
 
     Keys and values of a row's segment are always quantized whole, exactly as
@@ -226,7 +296,13 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     float64 [R, len(heads), D]; "zabs", per row the largest
     scale * sum_i |q8_i k8_i| over its keys, float64 [len(heads), R]; and
     "lse_flip" [len(heads), R] and "out_flip" [R, len(heads), D], how far
-    alternative roundings next to a midpoint can move lse and out.
+    alternative roundings next to a midpoint (and skip decisions next to the
+    threshold) can move lse and out; "skipped" [len(heads), R], the share of
+    the row's key tiles left out.
+
+    skip_threshold: apply the Skip-Softmax rule above (None or 0: every tile
+    counts).  Each requested row's whole 32-row block is evaluated, since the
+    decision belongs to the block.
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -249,6 +325,7 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     zabs = np.zeros((len(heads), len(rows)), dtype=np.float64)
     lflip = np.zeros((len(heads), len(rows)), dtype=np.float64)
     oflip = np.zeros((len(rows), len(heads), D), dtype=np.float64)
+    skipped = np.zeros((len(heads), len(rows)), dtype=np.float64)
     for s in np.unique(seg_of):
         a, b = int(cu[s]), int(cu[s + 1])
         sel = np.nonzero(seg_of == s)[0]
@@ -257,26 +334,61 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
         kw = 2.0 * rotation_error_bound(k_seg, pos[a:b], theta, dims)
         vs = np.asarray(v[a:b][:, heads, :], dtype=np.float64)
         kq, kc, vq = _quantized_segment_kv(kr, kw, vs)
-        q_rows = np.asarray(q[rows[sel]][:, heads, :], dtype=np.float64)
-        qr = _to_f32(rope(q_rows, pos[rows[sel]], theta, dims))
-        qw = 2.0 * rotation_error_bound(q_rows, pos[rows[sel]], theta, dims)
+        # rows to evaluate: the requested ones, or with skipping their whole 32-row blocks
+        want = rows[sel] - a
+        if skip_threshold:
+            blocks = np.unique(want // SKIP_QUERY_BLOCK)
+            ev = np.concatenate([np.arange(bq * SKIP_QUERY_BLOCK, min(b - a, (bq + 1) * SKIP_QUERY_BLOCK))
+                                 for bq in blocks])
+        else:
+            ev = want
+        q_rows = np.asarray(q[a + ev][:, heads, :], dtype=np.float64)
+        qr = _to_f32(rope(q_rows, pos[a + ev], theta, dims))
+        qw = 2.0 * rotation_error_bound(q_rows, pos[a + ev], theta, dims)
         qq = np.empty_like(qr)
         qc = np.empty_like(qr)
         for i in range(qr.shape[0]):
             for j in range(qr.shape[1]):
                 qq[i, j], qc[i, j] = quantize_block_margin(qr[i, j], qw[i, j])
+        pos_in_ev = {int(r): i for i, r in enumerate(ev)}
+        pick = np.array([pos_in_ev[int(r)] for r in want])
+        S_seg = b - a
+        n_tiles = (S_seg + SKIP_KEY_TILE - 1) // SKIP_KEY_TILE
         for j in range(len(heads)):
-            for r0 in range(0, len(sel), 512):
-                part = sel[r0:r0 + 512]
-                o, l, (sg, za, lf, of) = _segment_head(qq[r0:r0 + 512, j, :], kq[:, j, :], vq[:, j, :], scale,
-                                                        quantize_p, qc[r0:r0 + 512, j, :], kc[:, j, :])
-                out[part, j, :] = o
-                lse[j, part] = l
-                sig[part, j, :] = sg
-                zabs[j, part] = za
-                lflip[j, part] = lf
-                oflip[part, j, :] = of
-    scales = {"sigma": sig, "zabs": zabs, "lse_flip": lflip, "out_flip": oflip}
+            keep = amb = None
+            if skip_threshold:
+                z = (qq[:, j, :] @ kq[:, j, :].T) * scale
+                za = (np.abs(qq[:, j, :]) @ np.abs(kq[:, j, :]).T).max(axis=1) * abs(scale)
+                dzmax = ((np.abs(qq[:, j, :]) @ kc[:, j, :].T + qc[:, j, :] @ np.abs(kq[:, j, :]).T)
+                         * abs(scale)).max(axis=1)
+                delta = 2.0 ** -14 * za + dzmax
+                keep = np.ones((len(ev), S_seg), dtype=bool)
+                amb = np.zeros((len(ev), n_tiles), dtype=bool)
+                for bq in np.unique(ev // SKIP_QUERY_BLOCK):
+                    in_b = (ev // SKIP_QUERY_BLOCK) == bq
+                    sk, am = skip_decisions(z[in_b], np.ones(int(in_b.sum()), dtype=bool), skip_threshold,
+                                            SKIP_KEY_TILE, delta[in_b])
+                    keys_off = np.repeat(sk, SKIP_KEY_TILE)[:S_seg]
+                    keep[np.ix_(in_b, keys_off)] = False
+                    amb[in_b] = am
+            for r0 in range(0, len(ev), 512):
+                part = slice(r0, r0 + 512)
+                o, l, (sg, za2, lf, of) = _segment_head(
+                    qq[part, j, :], kq[:, j, :], vq[:, j, :], scale, quantize_p, qc[part, j, :], kc[:, j, :],
+                    None if keep is None else keep[part], None if amb is None else amb[part], SKIP_KEY_TILE)
+                idx = np.arange(len(ev))[part]
+                sel_here = np.nonzero(np.isin(pick, idx))[0]
+                loc = pick[sel_here] - r0
+                out[sel[sel_here], j, :] = o[loc]
+                lse[j, sel[sel_here]] = l[loc]
+                sig[sel[sel_here], j, :] = sg[loc]
+                zabs[j, sel[sel_here]] = za2[loc]
+                lflip[j, sel[sel_here]] = lf[loc]
+                oflip[sel[sel_here], j, :] = of[loc]
+                if keep is not None:
+                    kept_tiles = keep[part][loc][:, ::SKIP_KEY_TILE].sum(axis=1)
+                    skipped[j, sel[sel_here]] = 1.0 - kept_tiles / n_tiles
+    scales = {"sigma": sig, "zabs": zabs, "lse_flip": lflip, "out_flip": oflip, "skipped": skipped}
     return (out, lse, scales) if error_scales else (out, lse)
 
 

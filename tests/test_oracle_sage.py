@@ -302,3 +302,110 @@ def test_quantize_block_margin():
     blk[0] = 448.0 * (1 + 1e-12)
     q, change = sage.quantize_block_margin(blk, np.full(4, 1e-6))
     assert np.all(change > 0)
+
+
+# ---- Skip-Softmax rule -----------------------------------------------------------------------
+
+
+def _skip_case(seed, n=200, h=1, qscale=3.0):
+    """Local attention: q_i . k_j = a^2 sum_m cos((i - j) w_m) + noise peaks at i = j, so tiles
+    far after a block's own keys carry almost no weight."""
+    rng = np.random.default_rng(seed)
+    w = 0.5 * np.power(10.0, -np.arange(D // 2) / (D // 2))
+    ang = np.arange(n)[:, None] * w[None, :]
+    f = np.concatenate([np.cos(ang), np.sin(ang)], axis=1) * qscale / 1.5
+    q = (f + 0.3 * rng.standard_normal((n, D)))[:, None, :].repeat(h, axis=1)
+    k = (f + 0.3 * rng.standard_normal((n, D)))[:, None, :].repeat(h, axis=1)
+    v = rng.standard_normal((n, h, D))
+    return q, k, v, np.zeros((n, 3)), np.array([0, n])
+
+
+def test_skip_with_negligible_threshold_is_dense():
+    q, k, v, pos, cu = _skip_case(20)
+    dense = sage.sage_attention(q, k, v, cu, pos)
+    tiny = sage.sage_attention(q, k, v, cu, pos, skip_threshold=1e-300)
+    assert np.array_equal(dense[0], tiny[0]) and np.array_equal(dense[1], tiny[1])
+
+
+def test_skip_drops_a_negligible_tile():
+    # Tile 1 (keys 64..127) points away from every query: its logits sit ~40 below tile 0's,
+    # so it is skipped and the rows equal attention over tile 0 alone.
+    rng = np.random.default_rng(21)
+    n = 128
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = (8.0 * u + 0.1 * rng.standard_normal((n, D)))[:, None, :]
+    k = np.empty((n, 1, D))
+    k[:64, 0] = 4.0 * u + 0.5 * rng.standard_normal((64, D))
+    k[64:, 0] = -4.0 * u + 0.5 * rng.standard_normal((64, D))
+    v = rng.standard_normal((n, 1, D))
+    pos = np.zeros((n, 3))
+    out, lse, es = sage.sage_attention(q, k, v, np.array([0, n]), pos, skip_threshold=0.05, error_scales=True)
+    ref_o, ref_l = sage.sage_attention_rows(q[:, :, :], np.concatenate([k[:64], k[:64]]),
+                                            np.concatenate([v[:64], np.zeros_like(v[:64])]),
+                                            np.array([0, 64, 128]), pos, np.arange(64))
+    # rows 0..63 against a segment holding only tile 0: same quantization of tile 0's blocks
+    assert np.allclose(out[:64], ref_o, rtol=0, atol=1e-12) and np.allclose(lse[:, :64], ref_l, rtol=0, atol=1e-12)
+    assert np.all(es["skipped"] == 0.5)
+
+
+def _brute_skip(q8, k8, v8, scale, thr):
+    """Loops: per 32-row block, per 64-key tile in order, the rule written out; exact softmax."""
+    R, S = q8.shape[0], k8.shape[0]
+    z = [[sum(q8[i, d] * k8[j, d] for d in range(D)) * scale for j in range(S)] for i in range(R)]
+    keep = [[True] * S for _ in range(R)]
+    for b0 in range(0, R, 32):
+        rows = range(b0, min(R, b0 + 32))
+        running = {i: -math.inf for i in rows}
+        for t0 in range(0, S, 64):
+            tmax = {i: max(z[i][t0:t0 + 64]) for i in rows}
+            if all(tmax[i] < running[i] + math.log(thr) for i in rows):
+                for i in rows:
+                    for j in range(t0, min(S, t0 + 64)):
+                        keep[i][j] = False
+            for i in rows:
+                running[i] = max(running[i], tmax[i])
+    out = np.zeros((R, D))
+    lse = np.zeros(R)
+    for i in range(R):
+        ks = [j for j in range(S) if keep[i][j]]
+        zm = max(z[i][j] for j in ks)
+        e = {j: math.exp(z[i][j] - zm) for j in ks}
+        tot = sum(e.values())
+        for d in range(D):
+            out[i, d] = sum(e[j] * v8[j, d] for j in ks) / tot
+        lse[i] = zm + math.log(tot)
+    return out, lse, keep
+
+
+def test_skip_matches_brute_force():
+    q, k, v, pos, cu = _skip_case(22, n=230, qscale=3.0)
+    out, lse, es = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, skip_threshold=0.05, error_scales=True)
+    # the same quantized operands, through the brute-force rule
+    q8 = sage.quantize_rows(q[:, 0])
+    k8 = sage.quantize_key_blocks(k[:, 0], 16)
+    v8 = sage.quantize_key_blocks(v[:, 0], 64)
+    bo, bl, keep = _brute_skip(q8, k8, v8, 1.0 / math.sqrt(D), 0.05)
+    assert np.max(np.abs(out[:, 0] - bo)) <= 1e-12 and np.max(np.abs(lse[0] - bl)) <= 1e-12
+    share = 1.0 - np.array([sum(keep[i][::64]) for i in range(len(keep))]) / 4.0
+    assert np.allclose(es["skipped"][0], share)
+    assert share.max() > 0                  # the case really skips something
+
+
+def test_skip_is_monotone_in_the_threshold_and_decided_per_block():
+    q, k, v, pos, cu = _skip_case(23, n=230, qscale=3.0)
+    shares = []
+    for thr in (1e-6, 1e-3, 0.05, 0.3):
+        _, _, es = sage.sage_attention(q, k, v, cu, pos, skip_threshold=thr, error_scales=True)
+        shares.append(es["skipped"][0])
+    for lo, hi in zip(shares, shares[1:]):
+        assert np.all(hi >= lo)
+    # every row of a 32-row block shares the block's decisions
+    for b0 in range(0, 230, 32):
+        assert np.all(shares[2][b0:b0 + 32] == shares[2][b0])
+    # one row that needs tile 1 keeps it for its whole block: give row 5 a key of tile 1 that it
+    # matches strongly
+    k2 = k.copy()
+    k2[70, 0] = q[5, 0] * 3.0
+    _, _, es2 = sage.sage_attention(q, k2, v, cu, pos, skip_threshold=0.05, error_scales=True)
+    assert es2["skipped"][0][0] <= shares[2][0]
