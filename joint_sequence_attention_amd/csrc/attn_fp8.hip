@@ -463,14 +463,14 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   };
 
   // Iteration t, B = t mod 2 (S(t) in sc[B], P(t-1) in pf[1 - B]), reading
-  // K(t+1) from kslot and V(t-1) from vslot:
-  // 8 MFMA slots.  Slots 0..3 issue O += V(t-1) P(t-1), one MFMA per 32-dim
-  // block of O^T, next to the exponentials of subtile 0 of tile t, which
-  // then settles; slots 4..7 issue S(t+1) in the order (subtile, half) =
-  // (0,0), (1,0), (0,1), (1,1), straight into sc[1 - (t & 1)], next to the
-  // exponentials of subtile 1, which then settles.  Two fragment registers
-  // alternate, each read one slot ahead of its MFMA (the first two at the
-  // start).  A scheduling fence after every slot keeps this order.
+  // K(t+1) from kslot and V(t-1) from vslot: 8 MFMA slots.  Slots 0..3 issue
+  // S(t+1) in the order (subtile, half) = (0,0), (1,0), (0,1), (1,1), straight
+  // into sc[1 - B] (consecutive pairs share the query operand); slots 4..7
+  // issue O += V(t-1) P(t-1), one MFMA per 32-dim block of O^T (all four
+  // share the probabilities).  Exponential unit j of tile t follows slot j,
+  // then tile t settles.  Two fragment registers alternate, each read one or
+  // two slots ahead of its MFMA (the first two at the start).  A scheduling
+  // fence after every slot keeps this order.
   auto region = [&](auto B, auto QK, auto PV, auto kslot, auto vslot, unsigned k0, unsigned k1, unsigned vsc)
                     __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
@@ -479,30 +479,17 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     i32x8 fr[2], pw;
     asm volatile("" : "=v"(pw));  // every word is written below; no need to clear it first
     float rs = 0.0f;
-    if (do_pv) {
-      fr[0] = vfrag(vslot, 0);
-      fr[1] = vfrag(vslot, 1);
-    } else if (do_qk) {
+    if (do_qk) {
       fr[0] = kfrag(kslot, 0, 0);
       fr[1] = kfrag(kslot, 1, 0);
+    } else if (do_pv) {
+      fr[0] = vfrag(vslot, 0);
+      fr[1] = vfrag(vslot, 1);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (do_pv) {
-        o[j] = mfma_pv(o[j], fr[j & 1], pf[1 - b], vsc);
-        // next fragment into the register this MFMA has read
-        if (j < 2) fr[j] = vfrag(vslot, j + 2);
-        else if (do_qk) fr[j - 2] = kfrag(kslot, j - 2, 0);
-      }
-      float p[4];
-      exp_unit(ic<b>(), j, p);
-      pack_unit(j, p, pw, rs);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 4; j < 8; ++j) {
       if (do_qk) {
-        const int u = j & 1, ks = (j - 4) >> 1;
+        const int u = j & 1, ks = j >> 1;
         f32x16 acc;
         if (ks == 0) {
 #pragma unroll
@@ -511,7 +498,22 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           acc = sc[1 - b][u];
         }
         sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u ? k1 : k0);
-        if (ks == 0) fr[u] = kfrag(kslot, u, 1);
+        // next fragment into the register this MFMA has read
+        if (j < 2)
+          fr[u] = kfrag(kslot, u, 1);
+        else if (do_pv)
+          fr[u] = vfrag(vslot, j - 2);
+      }
+      float p[4];
+      exp_unit(ic<b>(), j, p);
+      pack_unit(j, p, pw, rs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 4; j < 8; ++j) {
+      if (do_pv) {
+        o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
+        if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
       }
       float p[4];
       exp_unit(ic<b>(), j, p);
