@@ -57,10 +57,11 @@ constexpr float P_SHIFT = 4.0f;          // probabilities are stored as p * 2^4
 constexpr float LAZY_SUM = 256.0f;       // largest row sum of a tile's scaled probabilities left unrescaled
 constexpr int E8M0_ONE = 127;            // 8-bit exponent scale of 2^0
 
-// LDS layouts, XOR-swizzled so that 8 or 16 lanes reading one logical 16-byte
-// chunk of consecutive rows hit distinct banks.
+// LDS layouts, XOR-swizzled so that the 16-byte fragment reads of a wave hit
+// distinct banks (SQ_LDS_BANK_CONFLICT reads 0 for both access patterns on
+// gfx950; a value-row swizzle of ((d >> 1) ^ (d >> 3)) & 3 measured conflicts).
 __device__ __forceinline__ int k8_swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
-__device__ __forceinline__ int v8_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+__device__ __forceinline__ int v8_swz(int d) { return (d >> 2) & 3; }
 __device__ __forceinline__ int k8_lds_offset(int r, int c) { return r * 128 + 16 * (c ^ k8_swz(r)); }
 __device__ __forceinline__ int v8_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ v8_swz(d)); }
 
