@@ -142,7 +142,11 @@ ROTATION_ERROR = 2.0 ** -22          # fp32 rotation error coefficient (see the 
 
 
 def rotation_error_bound(x, pos, theta=10000.0, dims=(32, 48, 48)) -> np.ndarray:
-    """Per element of rope(x): 2^-22 (1 + |phi|)(|x0| + |x1|) over its rotation pair, float64 [N, H, D]."""
+    """Per element of rope(x): 2^-22 (1 + |phi|)(|x0| + |x1|) over its rotation pair, float64 [N, H, D].
+
+    A pair that turns by phi = 0 gets 0: sin 0 = 0 and cos 0 = 1 are exact in
+    float32, so x0 * 1 - x1 * 0 and x0 * 0 + x1 * 1 give the pair back unchanged.
+    """
     from .rope import rope_frequencies
     x = np.abs(np.asarray(x, dtype=np.float64))
     pos = np.asarray(pos, dtype=np.float64)
@@ -151,7 +155,7 @@ def rotation_error_bound(x, pos, theta=10000.0, dims=(32, 48, 48)) -> np.ndarray
     for axis, width in enumerate(dims):
         phi = pos[:, axis][:, None] * rope_frequencies(theta, width)[None, :]      # [N, width/2]
         pair = x[:, :, offset:offset + width:2] + x[:, :, offset + 1:offset + width:2]
-        b = ROTATION_ERROR * (1.0 + np.abs(phi))[:, None, :] * pair
+        b = np.where((phi == 0.0)[:, None, :], 0.0, ROTATION_ERROR * (1.0 + np.abs(phi))[:, None, :] * pair)
         out[:, :, offset:offset + width:2] = b
         out[:, :, offset + 1:offset + width:2] = b
         offset += width
@@ -298,7 +302,8 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     "lse_flip" [len(heads), R] and "out_flip" [R, len(heads), D], how far
     alternative roundings next to a midpoint (and skip decisions next to the
     threshold) can move lse and out; "skipped" [len(heads), R], the share of
-    the row's key tiles left out.
+    the row's key tiles left out, and "skip_ambiguous" [len(heads), R], how
+    many of its block's decisions could go either way.
 
     skip_threshold: apply the Skip-Softmax rule above (None or 0: every tile
     counts).  Each requested row's whole 32-row block is evaluated, since the
@@ -326,6 +331,7 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     lflip = np.zeros((len(heads), len(rows)), dtype=np.float64)
     oflip = np.zeros((len(rows), len(heads), D), dtype=np.float64)
     skipped = np.zeros((len(heads), len(rows)), dtype=np.float64)
+    ambiguous = np.zeros((len(heads), len(rows)), dtype=np.int64)
     for s in np.unique(seg_of):
         a, b = int(cu[s]), int(cu[s + 1])
         sel = np.nonzero(seg_of == s)[0]
@@ -355,27 +361,30 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
         S_seg = b - a
         n_tiles = (S_seg + SKIP_KEY_TILE - 1) // SKIP_KEY_TILE
         for j in range(len(heads)):
-            keep = amb = None
-            if skip_threshold:
-                z = (qq[:, j, :] @ kq[:, j, :].T) * scale
-                za = (np.abs(qq[:, j, :]) @ np.abs(kq[:, j, :]).T).max(axis=1) * abs(scale)
-                dzmax = ((np.abs(qq[:, j, :]) @ kc[:, j, :].T + qc[:, j, :] @ np.abs(kq[:, j, :]).T)
-                         * abs(scale)).max(axis=1)
-                delta = 2.0 ** -14 * za + dzmax
-                keep = np.ones((len(ev), S_seg), dtype=bool)
-                amb = np.zeros((len(ev), n_tiles), dtype=bool)
-                for bq in np.unique(ev // SKIP_QUERY_BLOCK):
-                    in_b = (ev // SKIP_QUERY_BLOCK) == bq
-                    sk, am = skip_decisions(z[in_b], np.ones(int(in_b.sum()), dtype=bool), skip_threshold,
-                                            SKIP_KEY_TILE, delta[in_b])
-                    keys_off = np.repeat(sk, SKIP_KEY_TILE)[:S_seg]
-                    keep[np.ix_(in_b, keys_off)] = False
-                    amb[in_b] = am
+            # 512-row chunks hold whole 32-row blocks: every block but a segment's last is full
             for r0 in range(0, len(ev), 512):
                 part = slice(r0, r0 + 512)
+                keep = amb = None
+                if skip_threshold:
+                    qp, qcp = qq[part, j, :], qc[part, j, :]
+                    z = (qp @ kq[:, j, :].T) * scale
+                    za = (np.abs(qp) @ np.abs(kq[:, j, :]).T).max(axis=1) * abs(scale)
+                    dzmax = ((np.abs(qp) @ kc[:, j, :].T + qcp @ np.abs(kq[:, j, :]).T) * abs(scale)).max(axis=1)
+                    delta = 2.0 ** -14 * za + dzmax
+                    evp = ev[part]
+                    keep = np.ones((len(evp), S_seg), dtype=bool)
+                    amb = np.zeros((len(evp), n_tiles), dtype=bool)
+                    for bq in np.unique(evp // SKIP_QUERY_BLOCK):
+                        in_b = (evp // SKIP_QUERY_BLOCK) == bq
+                        sk, am = skip_decisions(z[in_b], np.ones(int(in_b.sum()), dtype=bool), skip_threshold,
+                                                SKIP_KEY_TILE, delta[in_b])
+                        keys_off = np.repeat(sk, SKIP_KEY_TILE)[:S_seg]
+                        keep[np.ix_(in_b, keys_off)] = False
+                        amb[in_b] = am
+                    del z
                 o, l, (sg, za2, lf, of) = _segment_head(
-                    qq[part, j, :], kq[:, j, :], vq[:, j, :], scale, quantize_p, qc[part, j, :], kc[:, j, :],
-                    None if keep is None else keep[part], None if amb is None else amb[part], SKIP_KEY_TILE)
+                    qq[part, j, :], kq[:, j, :], vq[:, j, :], scale, quantize_p, qc[part, j, :], kc[:, j, :], keep,
+                    amb, SKIP_KEY_TILE)
                 idx = np.arange(len(ev))[part]
                 sel_here = np.nonzero(np.isin(pick, idx))[0]
                 loc = pick[sel_here] - r0
@@ -386,9 +395,11 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
                 lflip[j, sel[sel_here]] = lf[loc]
                 oflip[sel[sel_here], j, :] = of[loc]
                 if keep is not None:
-                    kept_tiles = keep[part][loc][:, ::SKIP_KEY_TILE].sum(axis=1)
+                    kept_tiles = keep[loc][:, ::SKIP_KEY_TILE].sum(axis=1)
                     skipped[j, sel[sel_here]] = 1.0 - kept_tiles / n_tiles
-    scales = {"sigma": sig, "zabs": zabs, "lse_flip": lflip, "out_flip": oflip, "skipped": skipped}
+                    ambiguous[j, sel[sel_here]] = amb[loc].sum(axis=1)
+    scales = {"sigma": sig, "zabs": zabs, "lse_flip": lflip, "out_flip": oflip, "skipped": skipped,
+              "skip_ambiguous": ambiguous}
     return (out, lse, scales) if error_scales else (out, lse)
 
 

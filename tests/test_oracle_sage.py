@@ -274,7 +274,10 @@ def test_rotation_error_bound_covers_float32_rotation():
         y[:, :, off:off + width:2] = x0 * c - x1 * s
         y[:, :, off + 1:off + width:2] = x0 * s + x1 * c
         off += width
-    assert np.all(np.abs(y - exact) <= sage.rotation_error_bound(x, pos))
+    bound = sage.rotation_error_bound(x, pos)
+    assert np.all(np.abs(y - exact) <= bound)
+    # pairs at angle 0 (position 0 on their axis) carry no error: there the bound is 0, and met exactly
+    assert (bound == 0).any() and np.all(y[bound == 0] == x[bound == 0])
 
 
 def test_quantize_block_margin():
