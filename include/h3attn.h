@@ -186,14 +186,26 @@ h3attn_status h3attn_varlen_attention(const void* q, const int32_t* cu_seqlens, 
  * ownership and error rules apply unchanged.  Only the workspace differs:
  * it must hold h3attn_varlen_fwd_fp8_workspace_size bytes (256-byte aligned)
  * and its contents on return are unspecified.
+ *
+ * Skip-Softmax (same recipe section: an optional lossy "sparse attention"
+ * with a direct threshold, 0.05 there).  skip_threshold in [0, 1); 0 computes
+ * every key.  Otherwise queries go in blocks of 32 rows and keys in tiles of
+ * 64, both counted from the segment start; a block leaves a tile out when
+ * every row of the block has its largest logit in the tile below
+ * ln(skip_threshold) plus its largest logit over the earlier tiles, and out
+ * and lse are then softmax over the kept tiles.  Whether to use it for a
+ * given denoising step (the recipe keeps the early, high-noise steps dense)
+ * is the caller's choice.  skip_stats: NULL, or device uint64[2] to which the
+ * call adds the (block, tile) pairs it saw and those it left out; the caller
+ * clears it.  Fails with INVALID_ARG for a threshold outside [0, 1).
  * ------------------------------------------------------------------- */
 size_t h3attn_varlen_fwd_fp8_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs);
 
 h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                                     const float* pos_thw, void* out, float* lse, int64_t n_tokens, int32_t n_heads,
                                     int32_t head_dim, int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
-                                    const h3attn_rope_cfg* rope, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    float skip_threshold, const h3attn_rope_cfg* rope, void* workspace,
+                                    size_t workspace_bytes, uint64_t* skip_stats, void* stream);
 
 /* The two stages of h3attn_varlen_fwd_fp8, with the same contract as the
  * exact mode's pair: kv_prologue_fp8 rotates k, quantizes k and v and packs
@@ -208,8 +220,8 @@ h3attn_status h3attn_varlen_kv_prologue_fp8(const void* k, const void* v, const 
 h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqlens, const float* pos_thw, void* out,
                                           float* lse, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                                           int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
-                                          const h3attn_rope_cfg* rope, const void* workspace,
-                                          size_t workspace_bytes, void* stream);
+                                          float skip_threshold, const h3attn_rope_cfg* rope, const void* workspace,
+                                          size_t workspace_bytes, uint64_t* skip_stats, void* stream);
 
 /* Status name ("H3ATTN_OK", ...); never NULL. */
 const char* h3attn_status_string(h3attn_status s);

@@ -298,8 +298,8 @@ h3attn_status h3attn_varlen_kv_prologue_fp8(const void* k, const void* v, const 
 h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqlens, const float* pos_thw, void* out,
                                           float* lse, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                                           int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
-                                          const h3attn_rope_cfg* rope, const void* workspace,
-                                          size_t workspace_bytes, void* stream) {
+                                          float skip_threshold, const h3attn_rope_cfg* rope, const void* workspace,
+                                          size_t workspace_bytes, uint64_t* skip_stats, void* stream) {
   try {
     clear_error();
     h3attn_status st = check_varlen(n_tokens, n_heads, head_dim, n_seqs, max_seqlen);
@@ -308,6 +308,8 @@ h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqle
     st = make_rope_table(rope, head_dim, &table);
     if (st != H3ATTN_OK) return st;
     if (!std::isfinite(softmax_scale)) return fail(H3ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f))
+      return fail(H3ATTN_ERR_INVALID_ARG, "skip_threshold must lie in [0, 1)");
     if (n_tokens == 0) return H3ATTN_OK;
     if (!q || !cu_seqlens || !pos_thw || !out || !lse)
       return fail(H3ATTN_ERR_INVALID_ARG, "q, cu_seqlens, pos_thw, out and lse must be non-NULL");
@@ -320,9 +322,10 @@ h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqle
     const WorkspaceLayoutFp8 wl = workspace_layout_fp8(n_tokens, n_heads, n_seqs);
     const char* ws = static_cast<const char*>(workspace);
     return hip_status(launch_attention_fp8(q, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, n_seqs, max_seqlen,
-                                           scale, table, ws + wl.keys_offset, ws + wl.values_offset,
+                                           scale, skip_threshold, table, ws + wl.keys_offset, ws + wl.values_offset,
                                            reinterpret_cast<const unsigned*>(ws + wl.kscale_offset),
-                                           reinterpret_cast<const unsigned*>(ws + wl.vscale_offset), rows, stream));
+                                           reinterpret_cast<const unsigned*>(ws + wl.vscale_offset), rows,
+                                           reinterpret_cast<unsigned long long*>(skip_stats), stream));
   } catch (...) {
     return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_attention_fp8");
   }
@@ -331,8 +334,8 @@ h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqle
 h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                                     const float* pos_thw, void* out, float* lse, int64_t n_tokens, int32_t n_heads,
                                     int32_t head_dim, int32_t n_seqs, int32_t max_seqlen, float softmax_scale,
-                                    const h3attn_rope_cfg* rope, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    float skip_threshold, const h3attn_rope_cfg* rope, void* workspace,
+                                    size_t workspace_bytes, uint64_t* skip_stats, void* stream) {
   try {
     clear_error();
     // Check everything both stages need before launching the first one.
@@ -342,6 +345,8 @@ h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v,
     st = make_rope_table(rope, head_dim, &table);
     if (st != H3ATTN_OK) return st;
     if (!std::isfinite(softmax_scale)) return fail(H3ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f))
+      return fail(H3ATTN_ERR_INVALID_ARG, "skip_threshold must lie in [0, 1)");
     if (n_tokens == 0) return H3ATTN_OK;
     if (!q || !k || !v || !cu_seqlens || !pos_thw || !out || !lse)
       return fail(H3ATTN_ERR_INVALID_ARG, "q, k, v, cu_seqlens, pos_thw, out and lse must be non-NULL");
@@ -353,7 +358,8 @@ h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v,
                                        rope, workspace, workspace_bytes, stream);
     if (st != H3ATTN_OK) return st;
     return h3attn_varlen_attention_fp8(q, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, head_dim, n_seqs,
-                                       max_seqlen, softmax_scale, rope, workspace, workspace_bytes, stream);
+                                       max_seqlen, softmax_scale, skip_threshold, rope, workspace, workspace_bytes,
+                                       skip_stats, stream);
   } catch (...) {
     return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_fwd_fp8");
   }

@@ -38,6 +38,7 @@
 // unrounded fp32 probabilities.
 
 #include <atomic>
+#include <cmath>
 
 #include "device_common.h"
 
@@ -212,11 +213,13 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
 // V(t+3); iterations pair up into epochs that end with one barrier, exactly
 // as in the bf16 kernel.
 // ---------------------------------------------------------------------------
+template <bool SKIP>
 __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const char* __restrict__ k_ws, const char* __restrict__ v_ws,
-    const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_sc, int64_t rows_per_head) {
+    const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_sc, int64_t rows_per_head, float skip_log2,
+    unsigned long long* __restrict__ skip_stats) {
   static_assert(F8_TILE_BYTES / 16 == F8_NW * 64, "one direct load per lane, tile and tensor");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -343,6 +346,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mm = -INFINITY, l = 0.0f;
+  float mt = -INFINITY;        // Skip-Softmax: largest base-2 logit of the tiles seen so far
+  unsigned n_seen = 0, n_skipped = 0;
   f32x16 sc[2][2];          // S^T of one tile [buffer by tile parity][subtile]
   i32x8 pf[2];              // its e4m3 probabilities, by tile parity
 
@@ -472,8 +477,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // then tile t settles.  Two fragment registers alternate, each read one or
   // two slots ahead of its MFMA (the first two at the start).  A scheduling
   // fence after every slot keeps this order.
-  auto region = [&](auto B, auto QK, auto PV, auto kslot, auto vslot, unsigned k0, unsigned k1, unsigned vsc)
-                    __attribute__((always_inline)) {
+  auto region = [&](auto B, auto QK, auto PV, bool do_exp, auto kslot, auto vslot, unsigned k0, unsigned k1,
+                    unsigned vsc) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     constexpr bool do_qk = decltype(QK)::value != 0;
     constexpr bool do_pv = decltype(PV)::value != 0;
@@ -505,9 +510,11 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         else if (do_pv)
           fr[u] = vfrag(vslot, j - 2);
       }
-      float p[4];
-      exp_unit(ic<b>(), j, p);
-      pack_unit(j, p, pw, rs);
+      if (do_exp) {
+        float p[4];
+        exp_unit(ic<b>(), j, p);
+        pack_unit(j, p, pw, rs);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -516,13 +523,46 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
         if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
       }
-      float p[4];
-      exp_unit(ic<b>(), j, p);
-      pack_unit(j, p, pw, rs);
+      if (do_exp) {
+        float p[4];
+        exp_unit(ic<b>(), j, p);
+        pack_unit(j, p, pw, rs);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    settle(ic<b>(), pw, rs);
-    pf[b] = pw;
+    if (do_exp) {
+      settle(ic<b>(), pw, rs);
+      pf[b] = pw;
+    } else {
+      // a skipped tile: its products still run, on zero probabilities
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[b][j] = 0;
+    }
+  };
+
+  // Skip-Softmax decision for tile t (scores in buffer B): the wave leaves the
+  // tile out when each of its rows has a tile maximum below its running
+  // maximum of earlier tiles times the threshold (rows past the segment end
+  // do not vote).  Updates the running maximum; returns the uniform decision.
+  auto decide = [&](auto B) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    float mx = sc[b][0][0];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
+    const float tm = pair_max(mx) * cq;
+    const bool lets_go = qrow >= S || tm < mt + skip_log2;
+    mt = fmaxf(mt, tm);
+    return __builtin_amdgcn_ballot_w64(!lets_go) == 0;
+  };
+  // Iteration t under Skip-Softmax: the exponentials of tile t only if the
+  // wave keeps it (a skipped tile's products run on zero probabilities).
+  auto region_skip = [&](auto B, auto QK, auto kslot, auto vslot, unsigned k0, unsigned k1, unsigned vsc, bool skip)
+      __attribute__((always_inline)) {
+    region(B, QK, ic<1>(), !skip, kslot, vslot, k0, k1, vsc);
+    ++n_seen;
+    n_skipped += skip ? 1u : 0u;
   };
 
   // Scales for the products iteration t issues: K(t+1) and V(t-1).
@@ -536,7 +576,10 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // the ring barrier counts.
   auto step = [&](auto T8, int t) __attribute__((always_inline)) {
     constexpr int t8 = decltype(T8)::value;
-    region(ic<t8 & 1>(), ic<1>(), ic<1>(), ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq);
+    if constexpr (SKIP)
+      region_skip(ic<t8 & 1>(), ic<1>(), ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq, decide(ic<t8 & 1>()));
+    else
+      region(ic<t8 & 1>(), ic<1>(), ic<1>(), true, ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq);
     load_k(min(t + 5, last_t), ic<(t8 + 5) & 7>());
     load_v(min(t + 3, last_t), ic<(t8 + 3) & 7>());
     kscales(min(t + 2, last_t), kq0, kq1);
@@ -549,7 +592,10 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   auto last = [&](auto B) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     mask_tail(ic<b>(), last_t);
-    region(ic<b>(), ic<0>(), ic<1>(), 0, (last_t - 1) & 7, kq0, kq1, vq);
+    if constexpr (SKIP)
+      region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, vq, decide(ic<b>()));
+    else
+      region(ic<b>(), ic<0>(), ic<1>(), true, 0, (last_t - 1) & 7, kq0, kq1, vq);
     const unsigned vl = vscale(last_t);
     ring_barrier<0>();  // V(t) has landed
     __builtin_amdgcn_sched_barrier(0);
@@ -562,7 +608,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   }
   if (n_kt == 1) {
     mask_tail(ic<0>(), 0);
-    region(ic<0>(), ic<0>(), ic<0>(), ic<1>(), ic<7>(), 0u, 0u, 0u);
+    if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept; this seeds the running maximum
+    region(ic<0>(), ic<0>(), ic<0>(), true, ic<1>(), ic<7>(), 0u, 0u, 0u);
     const unsigned vl = vscale(0);
     ring_barrier<0>();
     pv_alone(ic<0>(), ic<0>(), vl);
@@ -570,7 +617,11 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     ring_barrier<6>();  // every wave is done with K(0) before its slot is refilled
     kscales(1, kq0, kq1);
     // t = 0: no products of an earlier tile yet; an epoch of its own.
-    region(ic<0>(), ic<1>(), ic<0>(), ic<1>(), ic<7>(), kq0, kq1, 0u);
+    if constexpr (SKIP) {
+      (void)decide(ic<0>());  // the first tile is always kept; this seeds the running maximum
+      ++n_seen;
+    }
+    region(ic<0>(), ic<1>(), ic<0>(), true, ic<1>(), ic<7>(), kq0, kq1, 0u);
     load_k(min(5, last_t), ic<5>());
     load_v(min(3, last_t), ic<3>());
     kscales(min(2, last_t), kq0, kq1);
@@ -622,6 +673,13 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       }
     if (g == 0) lse[int64_t(h) * n_tokens + tok] = (mm + log2f(lt)) * 0.69314718055994531f;
   }
+  if constexpr (SKIP) {
+    // tiles seen and left out by this wave (if any of its rows exists), for callers that ask
+    if (skip_stats != nullptr && lane == 0 && qt * F8_BQ + wave * 32 < S) {
+      atomicAdd(&skip_stats[0], (unsigned long long)(n_kt == 1 ? 1u : n_seen));
+      atomicAdd(&skip_stats[1], (unsigned long long)n_skipped);
+    }
+  }
 }
 }  // namespace
 
@@ -639,27 +697,39 @@ int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, cons
 
 int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
                          int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
-                         const RopeTable& table, const void* k_ws, const void* v_ws, const unsigned* k_sc,
-                         const unsigned* v_sc, int64_t rows_per_head, void* stream) {
+                         float skip_threshold, const RopeTable& table, const void* k_ws, const void* v_ws,
+                         const unsigned* k_sc, const unsigned* v_sc, int64_t rows_per_head,
+                         unsigned long long* skip_stats, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + F8_BQ - 1) / F8_BQ);
   if (tiles == 0) return 0;
-  // The dynamic LDS limit is raised once per device.
+  const bool skip = skip_threshold > 0.0f;
+  const void* fn = skip ? reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<true>)
+                        : reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<false>);
+  // The dynamic LDS limit is raised once per device and kernel instance.
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return int(e);
-  static std::atomic<uint64_t> attr_set{0};
+  static std::atomic<uint64_t> attr_set[2] = {0, 0};
   const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
-  if (bit == 0 || (attr_set.load(std::memory_order_acquire) & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_fp8_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(F8_SMEM));
+  if (bit == 0 || (attr_set[skip].load(std::memory_order_acquire) & bit) == 0) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(F8_SMEM));
     if (e != hipSuccess) return int(e);
-    attr_set.fetch_or(bit, std::memory_order_acq_rel);
+    attr_set[skip].fetch_or(bit, std::memory_order_acq_rel);
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_fp8_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(F8_NW * 64),
-                     F8_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu, pos,
-                     static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
-                     static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_sc, rows_per_head);
+  const float skip_log2 = skip ? std::log2(skip_threshold) : 0.0f;
+  const dim3 grid(tiles, unsigned(n_seqs), unsigned(n_heads));
+  if (skip)
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, grid, dim3(F8_NW * 64), F8_SMEM, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(q), cu, pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens),
+                       n_heads, scale_log2, table, static_cast<const char*>(k_ws), static_cast<const char*>(v_ws),
+                       k_sc, v_sc, rows_per_head, skip_log2, skip_stats);
+  else
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, grid, dim3(F8_NW * 64), F8_SMEM,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu, pos,
+                       static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
+                       static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_sc, rows_per_head,
+                       0.0f, nullptr);
   return int(hipGetLastError());
 }
 

@@ -88,8 +88,9 @@ int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, cons
                            unsigned* k_sc, unsigned* v_sc, int64_t rows_per_head, void* stream);
 int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
                          int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
-                         const RopeTable& table, const void* k_ws, const void* v_ws, const unsigned* k_sc,
-                         const unsigned* v_sc, int64_t rows_per_head, void* stream);
+                         float skip_threshold, const RopeTable& table, const void* k_ws, const void* v_ws,
+                         const unsigned* k_sc, const unsigned* v_sc, int64_t rows_per_head,
+                         unsigned long long* skip_stats, void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace h3attn

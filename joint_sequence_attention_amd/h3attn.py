@@ -88,11 +88,13 @@ def lib():
     L.h3attn_varlen_fwd_fp8_workspace_size.restype = c_sz
     L.h3attn_varlen_fwd_fp8_workspace_size.argtypes = [c_i64, c_i32, c_i32, c_i32]
     L.h3attn_varlen_fwd_fp8.restype = ctypes.c_int
-    L.h3attn_varlen_fwd_fp8.argtypes = list(L.h3attn_varlen_fwd.argtypes)
+    L.h3attn_varlen_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.c_float,
+                                        ctypes.c_float, rp, vp, c_sz, vp, vp]
     L.h3attn_varlen_kv_prologue_fp8.restype = ctypes.c_int
     L.h3attn_varlen_kv_prologue_fp8.argtypes = list(L.h3attn_varlen_kv_prologue.argtypes)
     L.h3attn_varlen_attention_fp8.restype = ctypes.c_int
-    L.h3attn_varlen_attention_fp8.argtypes = list(L.h3attn_varlen_attention.argtypes)
+    L.h3attn_varlen_attention_fp8.argtypes = [vp, vp, vp, vp, vp, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.c_float,
+                                              ctypes.c_float, rp, vp, c_sz, vp, vp]
     _lib = L
     return L
 
@@ -295,9 +297,21 @@ def h3attn_varlen_attention(q, cu_seqlens, pos_thw, max_seqlen, workspace, out=N
     return out, lse
 
 
+def _skip_stats_ptr(skip_stats):
+    if skip_stats is None:
+        return None
+    torch = _torch()
+    _need(skip_stats, torch.int64, (2,), "skip_stats")
+    return skip_stats.data_ptr()
+
+
 def h3attn_varlen_fwd_fp8(q, k, v, cu_seqlens, pos_thw, max_seqlen, out=None, lse=None, softmax_scale=0.0,
-                          theta=DEFAULT_THETA, dims=DEFAULT_DIMS, workspace=None, stream=None):
-    """Lossy FP8 (SAGE-style) mode of h3attn_varlen_fwd; same arguments and results."""
+                          skip_threshold=0.0, theta=DEFAULT_THETA, dims=DEFAULT_DIMS, workspace=None, skip_stats=None,
+                          stream=None):
+    """Lossy FP8 (SAGE-style) mode of h3attn_varlen_fwd, optionally with Skip-Softmax; same results' layout.
+
+    skip_stats: None or an int64 tensor [2] on the GPU that the call adds (tiles seen, tiles skipped) to.
+    """
     torch = _torch()
     N, H, Dh, n_seqs = _varlen_common(q, cu_seqlens, pos_thw, max_seqlen)
     _need(k, torch.bfloat16, q.shape, "k")
@@ -313,8 +327,9 @@ def h3attn_varlen_fwd_fp8(q, k, v, cu_seqlens, pos_thw, max_seqlen, out=None, ls
     cfg = rope_cfg(theta, dims)
     _check(lib().h3attn_varlen_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                        pos_thw.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, Dh, n_seqs,
-                                       int(max_seqlen), float(softmax_scale), ctypes.byref(cfg),
-                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       int(max_seqlen), float(softmax_scale), float(skip_threshold),
+                                       ctypes.byref(cfg), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _skip_stats_ptr(skip_stats),
                                        _stream_ptr(stream)),
            "h3attn_varlen_fwd_fp8")
     return out, lse
@@ -335,7 +350,8 @@ def h3attn_varlen_kv_prologue_fp8(k, v, cu_seqlens, pos_thw, max_seqlen, workspa
 
 
 def h3attn_varlen_attention_fp8(q, cu_seqlens, pos_thw, max_seqlen, workspace, out=None, lse=None,
-                                softmax_scale=0.0, theta=DEFAULT_THETA, dims=DEFAULT_DIMS, stream=None):
+                                softmax_scale=0.0, skip_threshold=0.0, theta=DEFAULT_THETA, dims=DEFAULT_DIMS,
+                                skip_stats=None, stream=None):
     torch = _torch()
     N, H, Dh, n_seqs = _varlen_common(q, cu_seqlens, pos_thw, max_seqlen)
     if out is None:
@@ -347,8 +363,9 @@ def h3attn_varlen_attention_fp8(q, cu_seqlens, pos_thw, max_seqlen, workspace, o
     cfg = rope_cfg(theta, dims)
     _check(lib().h3attn_varlen_attention_fp8(q.data_ptr(), cu_seqlens.data_ptr(), pos_thw.data_ptr(),
                                              out.data_ptr(), lse.data_ptr(), N, H, Dh, n_seqs, int(max_seqlen),
-                                             float(softmax_scale), ctypes.byref(cfg), workspace.data_ptr(),
-                                             workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+                                             float(softmax_scale), float(skip_threshold), ctypes.byref(cfg),
+                                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                             _skip_stats_ptr(skip_stats), _stream_ptr(stream)),
            "h3attn_varlen_attention_fp8")
     return out, lse
 

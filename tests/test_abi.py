@@ -123,12 +123,14 @@ def _cfg(theta=10000.0, dims=(32, 48, 48)):
 
 
 def _fwd(L, q=FAKE, k=FAKE * 2, v=FAKE * 3, cu=FAKE * 4, pos=FAKE * 5, out=1 << 40, lse=1 << 41, N=64, Hh=2,
-         Dh=128, ns=1, ms=64, scale=0.0, cfg=None, ws=1 << 42, wsb=None, fp8=False):
+         Dh=128, ns=1, ms=64, scale=0.0, cfg=None, ws=1 << 42, wsb=None, fp8=False, skip=0.0):
     size = L.h3attn_varlen_fwd_fp8_workspace_size if fp8 else L.h3attn_varlen_fwd_workspace_size
-    fwd = L.h3attn_varlen_fwd_fp8 if fp8 else L.h3attn_varlen_fwd
     if wsb is None:
         wsb = size(N, Hh, 128, ns)
-    return fwd(q, k, v, cu, pos, out, lse, N, Hh, Dh, ns, ms, scale, cfg or _cfg(), ws, wsb, None)
+    if fp8:
+        return L.h3attn_varlen_fwd_fp8(q, k, v, cu, pos, out, lse, N, Hh, Dh, ns, ms, scale, skip, cfg or _cfg(), ws,
+                                       wsb, None, None)
+    return L.h3attn_varlen_fwd(q, k, v, cu, pos, out, lse, N, Hh, Dh, ns, ms, scale, cfg or _cfg(), ws, wsb, None)
 
 
 @pytest.mark.parametrize(
@@ -218,9 +220,13 @@ def test_fp8_stage_argument_checks(L):
     wsb = L.h3attn_varlen_fwd_fp8_workspace_size(64, 2, 128, 1)
     assert L.h3attn_varlen_kv_prologue_fp8(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, 64, 2, 128, 1, 64, _cfg(), 1 << 42,
                                            wsb - 1, None) == H.H3ATTN_ERR_WORKSPACE
-    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, 1 << 40, 1 << 41, 64, 2, 128, 1, 64, 0.0, _cfg(),
-                                         1 << 42, wsb - 1, None) == H.H3ATTN_ERR_WORKSPACE
-    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, FAKE, 1 << 41, 64, 2, 128, 1, 64, 0.0, _cfg(),
-                                         1 << 42, wsb, None) == H.H3ATTN_ERR_INVALID_ARG   # out overlaps q
+    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, 1 << 40, 1 << 41, 64, 2, 128, 1, 64, 0.0, 0.0,
+                                         _cfg(), 1 << 42, wsb - 1, None, None) == H.H3ATTN_ERR_WORKSPACE
+    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, FAKE, 1 << 41, 64, 2, 128, 1, 64, 0.0, 0.0,
+                                         _cfg(), 1 << 42, wsb, None, None) == H.H3ATTN_ERR_INVALID_ARG   # out overlaps q
+    for bad in (-0.1, 1.0, float("nan"), float("inf")):
+        assert _fwd(L, fp8=True, skip=bad) == H.H3ATTN_ERR_INVALID_ARG
+        assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, 1 << 40, 1 << 41, 64, 2, 128, 1, 64, 0.0, bad,
+                                             _cfg(), 1 << 42, wsb, None, None) == H.H3ATTN_ERR_INVALID_ARG
     assert L.h3attn_varlen_kv_prologue_fp8(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, 64, 2, 64, 1, 64, _cfg(), 1 << 42,
                                            wsb, None) == H.H3ATTN_ERR_UNSUPPORTED

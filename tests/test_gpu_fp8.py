@@ -155,3 +155,84 @@ def test_fp8_many_heads_full(gpu):
     c = Case([[wl.visual(2, 16, 16)]], 128, seed=173)
     say(f"fp8 128 heads: N={c.N} H=128")
     _full(c, "128 heads")
+
+
+# ---- Skip-Softmax ------------------------------------------------------------------------------
+
+
+def _local_case(n_tokens, heads, seed, sharp=3.0):
+    """A sequence whose attention is local: q_i . k_j peaks at i = j (features cos/sin of i w_m),
+    positions zero (identity rotation), so tiles far after a block's own keys carry almost no weight."""
+    from helpers import bits_to_device
+    rng = np.random.default_rng(seed)
+    w = 0.5 * np.power(10.0, -np.arange(64) / 64.0)
+    ang = np.arange(n_tokens)[:, None] * w[None, :]
+    f = np.concatenate([np.cos(ang), np.sin(ang)], axis=1) * sharp / 1.5
+    def bits(x):
+        return wl._round_bf16_bits(np.ascontiguousarray(x, dtype=np.float32))
+    q = f[:, None, :] + 0.3 * rng.standard_normal((n_tokens, heads, 128))
+    k = f[:, None, :] + 0.3 * rng.standard_normal((n_tokens, heads, 128))
+    v = rng.standard_normal((n_tokens, heads, 128))
+    c = Case([[wl.visual(1, 1, n_tokens)]], heads, seed)
+    c.qb, c.kb, c.vb = bits(q), bits(k), bits(v)
+    dev = c.q.device
+    c.q, c.k, c.v = bits_to_device(c.qb, dev), bits_to_device(c.kb, dev), bits_to_device(c.vb, dev)
+    c.pos = np.zeros_like(c.pos)
+    c.pos_d = c.pos_d.zero_()
+    return c
+
+
+def _skip_run(c, thr, rows=None, label=""):
+    import torch
+    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out, lse = c.run_fp8(skip_threshold=thr, skip_stats=stats)
+    o64, l64 = device_to_f64(out), device_to_f64(lse)
+    o_s, l_s, es = c.sage_rows(rows, skip_threshold=thr)
+    o_e, l_e = (c.oracle_full() if rows is None else c.oracle_rows(rows))
+    if rows is not None:
+        o64, l64 = o64[rows], l64[:, rows]
+    compare_fp8(o64, l64, o_s, l_s, es, o_e, l_e, label=label, exact_bars=False)
+    seen, skipped = (int(x) for x in stats.cpu().numpy())
+    say(f"{label}: kernel left out {skipped} of {seen} (block, tile) pairs; oracle share {es['skipped'].mean():.4f}")
+    return seen, skipped, es
+
+
+def test_fp8_skip_negligible_threshold_equals_dense(gpu):
+    import torch
+    c = Case(ragged_segments(), 3, 180)
+    out, lse = c.run_fp8()
+    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out2, lse2 = c.run_fp8(skip_threshold=1e-30, skip_stats=stats)
+    assert np.array_equal(bf16_bits(out), bf16_bits(out2))
+    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+    seen, skipped = (int(x) for x in stats.cpu().numpy())
+    assert skipped == 0 and seen > 0
+
+
+def test_fp8_skip_local_attention_full(gpu):
+    # local attention: most (block, tile) pairs are negligible; every row checked against the oracle's rule
+    c = _local_case(1000, 2, 181)
+    say(f"fp8 skip local: N={c.N} H=2")
+    seen, skipped, es = _skip_run(c, 0.05, label="skip local")
+    # the kernel skips exactly what the oracle's rule skips, up to decisions next to the threshold
+    blocks = np.arange(c.N)[::32]
+    n_tiles = (c.N + 63) // 64
+    want = int(round(float((es["skipped"][:, blocks] * n_tiles).sum())))
+    slack = int(es["skip_ambiguous"][:, blocks].sum())
+    assert seen == 2 * len(blocks) * n_tiles
+    assert abs(skipped - want) <= slack, (skipped, want, slack)
+    assert skipped > seen // 3                    # the case really exercises skipping
+
+
+def test_fp8_skip_peaky_ragged_full(gpu):
+    c = Case(ragged_segments(), 2, 182, qscale=4.0)
+    say(f"fp8 skip peaky: lens={c.lens.tolist()}")
+    _skip_run(c, 0.05, label="skip peaky")
+
+
+def test_fp8_skip_workload_sampled_rows(gpu):
+    cfg = wl.config("1344x768")
+    c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
+    rows = c.sample_rows(n_random=16, seed=183)
+    say(f"fp8 skip 1344x768: N={c.N} H={c.heads}, {len(rows)} rows (whole 32-row blocks evaluated)")
+    _skip_run(c, 0.05, rows=rows, label="skip 1344x768")

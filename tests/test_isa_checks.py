@@ -87,17 +87,23 @@ def test_fp8_mfma_and_no_packed_fp32(isa_fp8):
     assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", isa_fp8)
 
 
-def test_fp8_main_loop_has_no_spills_or_block_copies(isa_fp8):
-    blocks = _loop_blocks(isa_fp8, "attn_fwd_fp8_kernel")
+@pytest.mark.parametrize("instance", ["attn_fwd_fp8_kernelILb0E", "attn_fwd_fp8_kernelILb1E"])
+def test_fp8_main_loop_has_no_spills_or_block_copies(isa_fp8, instance):
+    # both instances (dense, and with Skip-Softmax) are free of spills in the loop; the dense one,
+    # the hot path, also of register-block copies (the Skip-Softmax instance clears a probability
+    # operand with a short run of moves when it leaves a tile out)
+    blocks = _loop_blocks(isa_fp8, instance)
     assert len(blocks) >= 8
     for bl in blocks:
         text = "\n".join(bl)
         assert "scratch_" not in text
+        if instance.endswith("ILb1E"):
+            continue
         # a run of register moves would be the register allocator copying an accumulator (or the
         # output block) from one set of registers to another on every iteration
         run = longest = 0
         for ln in bl:
-            if re.match(r"\s+v_mov_b(32|64)_e32\s+v", ln):
+            if re.match(r"\s+v_mov_b(32|64)_e32\s+v[\[\d:\]]+,\s*v", ln):   # register to register
                 run += 1
                 longest = max(longest, run)
             elif ln.strip() and not ln.strip().startswith(";"):
