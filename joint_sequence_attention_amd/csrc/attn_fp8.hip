@@ -348,6 +348,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   float mm = -INFINITY, l = 0.0f;
   float mt = -INFINITY;        // Skip-Softmax: largest base-2 logit of the tiles seen so far
   unsigned n_seen = 0, n_skipped = 0;
+  bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
   f32x16 sc[2][2];          // S^T of one tile [buffer by tile parity][subtile]
   i32x8 pf[2];              // its e4m3 probabilities, by tile parity
 
@@ -477,8 +478,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // then tile t settles.  Two fragment registers alternate, each read one or
   // two slots ahead of its MFMA (the first two at the start).  A scheduling
   // fence after every slot keeps this order.
-  auto region = [&](auto B, auto QK, auto PV, bool do_exp, auto kslot, auto vslot, unsigned k0, unsigned k1,
-                    unsigned vsc) __attribute__((always_inline)) {
+  auto region = [&](auto B, auto QK, auto PV, bool do_exp, bool pv_live, auto kslot, auto vslot, unsigned k0,
+                    unsigned k1, unsigned vsc) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     constexpr bool do_qk = decltype(QK)::value != 0;
     constexpr bool do_pv = decltype(PV)::value != 0;
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int j = 4; j < 8; ++j) {
       if (do_pv) {
-        o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
+        if (pv_live) o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
         if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
       }
       if (do_exp) {
@@ -533,10 +534,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     if (do_exp) {
       settle(ic<b>(), pw, rs);
       pf[b] = pw;
-    } else {
-      // a skipped tile: its products still run, on zero probabilities
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[b][j] = 0;
     }
   };
 
@@ -557,10 +554,11 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     return __builtin_amdgcn_ballot_w64(!lets_go) == 0;
   };
   // Iteration t under Skip-Softmax: the exponentials of tile t only if the
-  // wave keeps it (a skipped tile's products run on zero probabilities).
+  // wave keeps it, the products of tile t-1 only if it kept that one.
   auto region_skip = [&](auto B, auto QK, auto kslot, auto vslot, unsigned k0, unsigned k1, unsigned vsc, bool skip)
       __attribute__((always_inline)) {
-    region(B, QK, ic<1>(), !skip, kslot, vslot, k0, k1, vsc);
+    region(B, QK, ic<1>(), !skip, prev_kept, kslot, vslot, k0, k1, vsc);
+    prev_kept = !skip;
     ++n_seen;
     n_skipped += skip ? 1u : 0u;
   };
@@ -579,7 +577,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     if constexpr (SKIP)
       region_skip(ic<t8 & 1>(), ic<1>(), ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq, decide(ic<t8 & 1>()));
     else
-      region(ic<t8 & 1>(), ic<1>(), ic<1>(), true, ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq);
+      region(ic<t8 & 1>(), ic<1>(), ic<1>(), true, true, ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq);
     load_k(min(t + 5, last_t), ic<(t8 + 5) & 7>());
     load_v(min(t + 3, last_t), ic<(t8 + 3) & 7>());
     kscales(min(t + 2, last_t), kq0, kq1);
@@ -595,11 +593,11 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     if constexpr (SKIP)
       region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, vq, decide(ic<b>()));
     else
-      region(ic<b>(), ic<0>(), ic<1>(), true, 0, (last_t - 1) & 7, kq0, kq1, vq);
+      region(ic<b>(), ic<0>(), ic<1>(), true, true, 0, (last_t - 1) & 7, kq0, kq1, vq);
     const unsigned vl = vscale(last_t);
     ring_barrier<0>();  // V(t) has landed
     __builtin_amdgcn_sched_barrier(0);
-    pv_alone(ic<b>(), last_t & 7, vl);
+    if (prev_kept) pv_alone(ic<b>(), last_t & 7, vl);
   };
   {
     unsigned k0, k1;
@@ -609,7 +607,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   if (n_kt == 1) {
     mask_tail(ic<0>(), 0);
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept; this seeds the running maximum
-    region(ic<0>(), ic<0>(), ic<0>(), true, ic<1>(), ic<7>(), 0u, 0u, 0u);
+    region(ic<0>(), ic<0>(), ic<0>(), true, true, ic<1>(), ic<7>(), 0u, 0u, 0u);
     const unsigned vl = vscale(0);
     ring_barrier<0>();
     pv_alone(ic<0>(), ic<0>(), vl);
@@ -621,7 +619,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       (void)decide(ic<0>());  // the first tile is always kept; this seeds the running maximum
       ++n_seen;
     }
-    region(ic<0>(), ic<1>(), ic<0>(), true, ic<1>(), ic<7>(), kq0, kq1, 0u);
+    region(ic<0>(), ic<1>(), ic<0>(), true, true, ic<1>(), ic<7>(), kq0, kq1, 0u);
     load_k(min(5, last_t), ic<5>());
     load_v(min(3, last_t), ic<3>());
     kscales(min(2, last_t), kq0, kq1);

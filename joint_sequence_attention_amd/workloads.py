@@ -34,6 +34,16 @@ optionally multiplied by a per-tensor factor, then rounded to bfloat16 by
 round-to-nearest-even on the float32 bit pattern.  The result is returned as
 uint16 bit patterns so that neither side needs a bfloat16 dtype to agree on
 the exact input values.
+
+Local-attention inputs (``local_qkv``), for the Skip-Softmax mode: with the
+same generator, first one direction per head, ``c_h = g / |g|`` for
+``g = standard_normal((H, D), float64)``; then q and k as
+``amp * c_h + standard_normal((N, H, D), float32)`` and v as
+``standard_normal((N, H, D), float32)``, each rounded to bfloat16 as above.
+When q and k share a direction, the rotary score of a pair depends mostly on
+the difference of their positions and peaks where it is zero, so attention
+is local in (t, h, w).  This stands in for the locality of a trained DiT's
+attention maps, which random weights do not have.
 """
 
 from __future__ import annotations
@@ -135,6 +145,20 @@ def random_qkv(n: int, heads: int, seed: int, head_dim: int = HEAD_DIM, scale=(1
         x = rng.standard_normal((n, heads, head_dim), dtype=np.float32)
         if s != 1.0:
             x = x * np.float32(s)
+        out.append(_round_bf16_bits(x))
+    return tuple(out)
+
+
+def local_qkv(n: int, heads: int, seed: int, amp: float, head_dim: int = HEAD_DIM):
+    """Seeded bf16 q, k, v (uint16 bit patterns, [n, heads, head_dim]) whose attention is local."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g = rng.standard_normal((heads, head_dim))
+    c = (g / np.linalg.norm(g, axis=1, keepdims=True)).astype(np.float32)
+    out = []
+    for shared in (True, True, False):
+        x = rng.standard_normal((n, heads, head_dim), dtype=np.float32)
+        if shared:
+            x = x + np.float32(amp) * c[None, :, :]
         out.append(_round_bf16_bits(x))
     return tuple(out)
 
