@@ -223,6 +223,18 @@ h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqle
                                           float skip_threshold, const h3attn_rope_cfg* rope, const void* workspace,
                                           size_t workspace_bytes, uint64_t* skip_stats, void* stream);
 
+/* Skip-Softmax timestep gate (vLLM-Omni "MiniMax-H3" recipe, section
+ * "Attention Backends": disabled_until_timestep keeps the early, high-noise
+ * denoising steps dense by comparing a cutoff with the step's video sigma).
+ * Host only, no device work.  Writes to *threshold_out the skip_threshold to
+ * pass to the FP8 calls for a step at noise level sigma: 0 (dense) while
+ * sigma > disabled_until_timestep, else skip_threshold.  With the recipe's
+ * flow shift of 12 and 50 steps, cutoffs 0.99, 0.97 and 0.95 keep the first
+ * 6, 14 and 19 of the 49 forwards dense.  Fails with INVALID_ARG for a NULL
+ * threshold_out, a skip_threshold outside [0, 1) or a NaN cutoff or sigma. */
+h3attn_status h3attn_skip_gate(float skip_threshold, float disabled_until_timestep, float sigma,
+                               float* threshold_out);
+
 /* Status name ("H3ATTN_OK", ...); never NULL. */
 const char* h3attn_status_string(h3attn_status s);
 /* Reason for the last non-OK status returned on this thread ("" if none). */

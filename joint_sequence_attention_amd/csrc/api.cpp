@@ -365,4 +365,17 @@ h3attn_status h3attn_varlen_fwd_fp8(const void* q, const void* k, const void* v,
   }
 }
 
+h3attn_status h3attn_skip_gate(float skip_threshold, float disabled_until_timestep, float sigma,
+                               float* threshold_out) {
+  clear_error();
+  if (!threshold_out) return fail(H3ATTN_ERR_INVALID_ARG, "threshold_out is NULL");
+  if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f))
+    return fail(H3ATTN_ERR_INVALID_ARG, "skip_threshold must lie in [0, 1)");
+  if (std::isnan(disabled_until_timestep)) return fail(H3ATTN_ERR_INVALID_ARG, "disabled_until_timestep is NaN");
+  if (std::isnan(sigma)) return fail(H3ATTN_ERR_INVALID_ARG, "sigma is NaN");
+  // dense while the step's noise level is above the cutoff
+  *threshold_out = sigma > disabled_until_timestep ? 0.0f : skip_threshold;
+  return H3ATTN_OK;
+}
+
 }  // extern "C"

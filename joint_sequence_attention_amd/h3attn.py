@@ -95,6 +95,8 @@ def lib():
     L.h3attn_varlen_attention_fp8.restype = ctypes.c_int
     L.h3attn_varlen_attention_fp8.argtypes = [vp, vp, vp, vp, vp, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.c_float,
                                               ctypes.c_float, rp, vp, c_sz, vp, vp]
+    L.h3attn_skip_gate.restype = ctypes.c_int
+    L.h3attn_skip_gate.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float)]
     _lib = L
     return L
 
@@ -111,6 +113,7 @@ EXPORTED = (
     "h3attn_varlen_fwd_fp8",
     "h3attn_varlen_kv_prologue_fp8",
     "h3attn_varlen_attention_fp8",
+    "h3attn_skip_gate",
     "h3attn_status_string",
     "h3attn_last_error",
     "h3attn_abi_version",
@@ -214,6 +217,14 @@ def h3attn_rope_apply(x, pos_thw, out=None, theta=DEFAULT_THETA, dims=DEFAULT_DI
 
 def h3attn_varlen_fwd_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_seqs: int) -> int:
     return int(lib().h3attn_varlen_fwd_workspace_size(n_tokens, n_heads, head_dim, n_seqs))
+
+
+def h3attn_skip_gate(skip_threshold: float, disabled_until_timestep: float, sigma: float) -> float:
+    """The skip_threshold for a denoising step at noise level sigma: 0 (dense) above the cutoff."""
+    out = ctypes.c_float()
+    _check(lib().h3attn_skip_gate(float(skip_threshold), float(disabled_until_timestep), float(sigma),
+                                  ctypes.byref(out)), "h3attn_skip_gate")
+    return float(out.value)
 
 
 def h3attn_varlen_fwd_fp8_workspace_size(n_tokens: int, n_heads: int, head_dim: int, n_seqs: int) -> int:

@@ -26,7 +26,10 @@ What it computes (sources are the pages the method is described on):
   plus the natural-log log-sum-exp of each row.
 * ``sage``    -- the lossy FP8 mode of the same attention: Q and K in e4m3
   with one scale per query row and per 16 keys, P and V in e4m3 (vLLM-Omni
-  "MiniMax-H3" recipe, "Attention Backends", SAGE quantization).
+  "MiniMax-H3" recipe, "Attention Backends", SAGE quantization), with the
+  Skip-Softmax rule.
+* ``gate``    -- the Skip-Softmax timestep gate and the noise schedule of the
+  denoising steps it is compared with (same recipe section).
 
 Every function is pinned by tests under ``tests/`` against closed forms,
 invariants, brute force and library routines (see ``tests/test_oracle_*.py``).
@@ -38,6 +41,7 @@ from .layout import layout, round_half_even
 from .rope import rope, rope_frequencies
 from .attention import attention, attention_rows
 from .sage import round_e4m3, sage_attention, sage_attention_rows
+from .gate import flow_shift, forward_sigmas, skip_threshold_at
 
 __all__ = [
     "layout",
