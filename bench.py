@@ -15,6 +15,10 @@ workload, on this host's cores.
 fp8_mode: the same step through the lossy FP8 entry points (h3attn_varlen_fwd_fp8:
 e4m3 Q/K/P/V with block scales), with its own roofline against the fp8 dense
 MFMA peak.  It is reported beside the bf16 metric, never in its place.
+fp8_mode.skip_softmax: the FP8 attention kernel with Skip-Softmax at threshold
+0.05, against the dense FP8 kernel, both on seeded inputs whose attention is
+local (workloads.local_qkv); the share of (32-row block, 64-key tile) pairs
+left out is the kernel's own count.  effective_tflops counts the dense FLOP.
 """
 
 from __future__ import annotations
@@ -31,6 +35,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+SKIP_THRESHOLD = 0.05      # the recipe's Skip-Softmax threshold
+SKIP_AMPLITUDE = 20.0      # q/k amplitude of the local-attention inputs the skip mode is timed on
 
 # HBM bytes of one attn_fwd_kernel launch on the 1344x768 workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
@@ -300,6 +306,41 @@ def main():
            "roofline": {"bound": "mfma", "achieved": round(fp8_achieved, 2), "peak": PEAK_FP8_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(fp8_achieved / PEAK_FP8_TFLOPS, 4),
                         "kernel": "attn_fwd_fp8_kernel", "kernel_ms": round(fp8_attn_ms, 4)}}
+
+    # Skip-Softmax (FP8 mode, threshold 0.05 as in the recipe) on inputs whose attention is local:
+    # random N(0, 1) inputs give diffuse attention and no tile is ever left out.  The dense FP8
+    # kernel is timed on the same inputs.
+    lq, lk, lv = (dev_bf16(b) for b in wl.local_qkv(N, heads, cfg["seed"], SKIP_AMPLITUDE))
+
+    def time_fp8_attention(thr):
+        H.h3attn_varlen_kv_prologue_fp8(lk, lv, cu_d, pos_d, max_seqlen, ws8)
+        stats = torch.zeros(2, dtype=torch.int64, device=dev)
+        H.h3attn_varlen_attention_fp8(lq, cu_d, pos_d, max_seqlen, ws8, out=out, lse=lse, skip_threshold=thr,
+                                      skip_stats=stats)
+        for _ in range(max(0, args.warmup - 1)):
+            H.h3attn_varlen_attention_fp8(lq, cu_d, pos_d, max_seqlen, ws8, out=out, lse=lse, skip_threshold=thr)
+        torch.cuda.synchronize()
+        n_time = max(1, args.steps // 2)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_time)]
+        for a, b in ev:
+            a.record()
+            H.h3attn_varlen_attention_fp8(lq, cu_d, pos_d, max_seqlen, ws8, out=out, lse=lse, skip_threshold=thr)
+            b.record()
+        torch.cuda.synchronize()
+        seen, left = (int(x) for x in stats.cpu().tolist())
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])), (left / seen if seen else 0.0)
+
+    dense_ms, _ = time_fp8_attention(0.0)
+    skip_ms, skip_share = time_fp8_attention(SKIP_THRESHOLD)
+    print(f"[bench] skip-softmax {SKIP_THRESHOLD} on local-attention inputs: {skip_ms:.3f} ms vs dense fp8 "
+          f"{dense_ms:.3f} ms ({dense_ms / skip_ms:.3f}x), {100 * skip_share:.1f}% of (block, tile) pairs left out",
+          file=sys.stderr, flush=True)
+    fp8["skip_softmax"] = {
+        "threshold": SKIP_THRESHOLD,
+        "data": f"seeded local-attention q/k (shared direction per head, amplitude {SKIP_AMPLITUDE}), N(0,1) v",
+        "left_out": round(skip_share, 4), "kernel_ms": round(skip_ms, 4), "dense_kernel_ms": round(dense_ms, 4),
+        "speedup": round(dense_ms / skip_ms, 4),
+        "effective_tflops": round(flop / (skip_ms * 1e-3) / 1e12, 2)}
 
     cpu = None
     if not args.no_cpu_baseline:
