@@ -85,19 +85,26 @@ typedef struct h3attn_rope_cfg {
  * value rounded half to even (rule ROUND_HALF_EVEN); attached audio starts
  * where the preceding visual item started and leaves the clock alone, a
  * standalone audio item starts at the clock and advances it by span.
+ * A clock item emits no tokens and advances the clock by span: a long
+ * video's continuation chunk keeps its global temporal positions by putting
+ * one in front of its latents (vLLM-Omni "MiniMax-H3" recipe, "Long video
+ * and driving audio").  A text item emits n_audio tokens at (0, 0, 0) and
+ * leaves the clock alone: with every position 0 the rotation is the identity
+ * and the attention is plain softmax attention, the token refiner's short
+ * path (same recipe, "Attention Backends").
  * Positions are formed in double and rounded to float.
  * ------------------------------------------------------------------- */
-enum { H3ATTN_ITEM_VISUAL = 0, H3ATTN_ITEM_AUDIO = 1 };
+enum { H3ATTN_ITEM_VISUAL = 0, H3ATTN_ITEM_AUDIO = 1, H3ATTN_ITEM_CLOCK = 2, H3ATTN_ITEM_TEXT = 3 };
 enum { H3ATTN_AUDIO_LINEAR = 0, H3ATTN_AUDIO_ROUND_HALF_EVEN = 1 };
 
 typedef struct h3attn_item {
-  int32_t kind;     /* H3ATTN_ITEM_VISUAL or H3ATTN_ITEM_AUDIO */
-  int32_t T, H, W;  /* visual grid (each >= 1); ignored for audio */
-  int32_t n_audio;  /* audio rows (>= 0); ignored for visual */
+  int32_t kind;     /* H3ATTN_ITEM_VISUAL, _AUDIO, _CLOCK or _TEXT */
+  int32_t T, H, W;  /* visual grid (each >= 1); ignored otherwise */
+  int32_t n_audio;  /* audio or text rows (>= 0); ignored otherwise */
   int32_t attached; /* audio: 1 = soundtrack of the preceding visual item */
   int32_t rule;     /* audio: H3ATTN_AUDIO_LINEAR or H3ATTN_AUDIO_ROUND_HALF_EVEN */
   int32_t reserved; /* set to 0 */
-  double span;      /* audio: latent frames covered (finite, >= 0) */
+  double span;      /* audio: latent frames covered; clock: the advance (finite, >= 0) */
 } h3attn_item;
 
 /* items: host [sum(items_per_seq)]; items_per_seq: host [n_seqs] (>= 0 each);

@@ -5,7 +5,11 @@
 // "References"); each packed request is its own attention document with its
 // own clock (vLLM-Omni "MiniMax-H3" recipe, "Step execution and continuous
 // batching"); positions are formed in double and rounded to float for device
-// arithmetic ("MiniMax H3 on Moore Threads MUSA", "MUSA validation").
+// arithmetic ("MiniMax H3 on Moore Threads MUSA", "MUSA validation").  A clock
+// item moves the clock with no tokens, which places a long video's
+// continuation chunk at its global time (same recipe, "Long video and driving
+// audio"); a text item is a run of rows at position 0, the token refiner's
+// short attention path (same recipe, "Attention Backends").
 
 #include <cmath>
 #include <cstdint>
@@ -34,12 +38,22 @@ h3attn_status check_item(const h3attn_item& it) {
     if (it.attached != 0 && it.attached != 1) return h3attn::fail(H3ATTN_ERR_INVALID_ARG, "attached must be 0 or 1");
     return H3ATTN_OK;
   }
+  if (it.kind == H3ATTN_ITEM_CLOCK) {
+    if (!(std::isfinite(it.span) && it.span >= 0.0))
+      return h3attn::fail(H3ATTN_ERR_INVALID_ARG, "clock span must be finite and >= 0");
+    return H3ATTN_OK;
+  }
+  if (it.kind == H3ATTN_ITEM_TEXT) {
+    if (it.n_audio < 0) return h3attn::fail(H3ATTN_ERR_INVALID_ARG, "text item needs n_audio (its rows) >= 0");
+    return H3ATTN_OK;
+  }
   return h3attn::fail(H3ATTN_ERR_INVALID_ARG, "unknown item kind");
 }
 
 int64_t item_rows(const h3attn_item& it) {
   if (it.kind == H3ATTN_ITEM_VISUAL) return int64_t(it.T) * it.H * it.W;
-  return it.n_audio;
+  if (it.kind == H3ATTN_ITEM_CLOCK) return 0;
+  return it.n_audio;  // audio and text rows
 }
 
 }  // namespace
@@ -102,6 +116,11 @@ extern "C" h3attn_status h3attn_build_layout(const h3attn_item* items, const int
           }
           last_visual_start = clock;
           clock += it.T;
+        } else if (it.kind == H3ATTN_ITEM_CLOCK) {
+          clock += it.span;
+        } else if (it.kind == H3ATTN_ITEM_TEXT) {
+          if (pos_thw)
+            for (int64_t k = 0; k < 3 * int64_t(it.n_audio); ++k) pos_thw[3 * row + k] = 0.0f;
         } else {
           const double start = it.attached ? last_visual_start : clock;
           if (pos_thw) {

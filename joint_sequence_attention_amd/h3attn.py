@@ -26,6 +26,8 @@ H3ATTN_ERR_HIP = 4
 
 ITEM_VISUAL = 0
 ITEM_AUDIO = 1
+ITEM_CLOCK = 2
+ITEM_TEXT = 3
 AUDIO_LINEAR = 0
 AUDIO_ROUND_HALF_EVEN = 1
 
@@ -151,6 +153,10 @@ def _items(segments):
             elif it["kind"] == "audio":
                 rule = AUDIO_ROUND_HALF_EVEN if it["rule"] == "round" else AUDIO_LINEAR
                 flat.append(Item(ITEM_AUDIO, 0, 0, 0, it["n"], 1 if it["attached"] else 0, rule, 0, it["span"]))
+            elif it["kind"] == "clock":
+                flat.append(Item(ITEM_CLOCK, 0, 0, 0, 0, 0, 0, 0, it["span"]))
+            elif it["kind"] == "text":
+                flat.append(Item(ITEM_TEXT, 0, 0, 0, it["n"], 0, 0, 0, 0.0))
             else:
                 raise ValueError(f"unknown item kind {it['kind']!r}")
     items = (Item * max(1, len(flat)))(*flat)

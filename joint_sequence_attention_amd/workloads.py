@@ -18,6 +18,10 @@ Item vocabulary (one dict per item, items listed in reference order):
   before it (a video's own soundtrack); a standalone audio reference starts at
   the current clock and advances it by ``s``.  ``rule`` is ``"linear"``
   (offset i*s/n) or ``"round"`` (that offset rounded half-to-even).
+* ``{"kind": "clock", "span": s}`` -- no rows; moves the clock forward by
+  ``s`` (a long video's continuation chunk at its global time).
+* ``{"kind": "text", "n": n}`` -- ``n`` rows at position (0, 0, 0), e.g.
+  one prompt for the token refiner.
 
 The workloads follow the sequence structure the pages describe: the DiT packs
 the video latent and the audio latent into one long token sequence
@@ -64,6 +68,43 @@ def audio(n: int, span: float, attached: bool, rule: str = "linear") -> dict:
     return {"kind": "audio", "n": int(n), "span": float(span), "attached": bool(attached), "rule": rule}
 
 
+def clock(span: float) -> dict:
+    return {"kind": "clock", "span": float(span)}
+
+
+def text(n: int) -> dict:
+    return {"kind": "text", "n": int(n)}
+
+
+def native_frames(seconds: float, fps: int = 24) -> int:
+    """Frames of the native 17n+5 video-frame grid that cover ``seconds`` (the smallest n that does)."""
+    need = seconds * fps
+    n = max(0, -(-int(round(need - 5)) // 17))
+    return 17 * n + 5
+
+
+def latent_frames(frames: int) -> int:
+    """Latent frames of a 17n+5-frame video on the 5n+2 latent grid."""
+    assert (frames - 5) % 17 == 0
+    return 5 * ((frames - 5) // 17) + 2
+
+
+# Long video by latent continuation: the last chunk of a 300-second request (the continuation
+# limit), one image reference in front; the chunk keeps its global temporal positions.
+LONG_SECONDS = 300
+LONG_CHUNK = 17
+
+
+def _long_segment():
+    total = latent_frames(native_frames(LONG_SECONDS))
+    return [[visual(1, 24, 42), clock(total - LONG_CHUNK), visual(LONG_CHUNK, 24, 42),
+             audio(32 * LONG_CHUNK, LONG_CHUNK, attached=True)]]
+
+
+# Token refiner: eight co-batched prompts, each its own document.
+REFINER_PROMPTS = (77, 128, 203, 256, 300, 421, 512, 645)
+
+
 def _packed_segments():
     return [[visual(T, 24, 42), audio(32 * T, T, attached=True)] for T in (5, 9, 13, 17)]
 
@@ -103,9 +144,19 @@ CONFIGS = {
         "segments": _ref2va_segment(),
         "seed": 5,
     },
+    "long300": {
+        "heads": 24,
+        "segments": _long_segment(),
+        "seed": 6,
+    },
+    "refiner": {
+        "heads": 56,
+        "segments": [[text(n)] for n in REFINER_PROMPTS],
+        "seed": 7,
+    },
 }
 
-CONFIG_ORDER = ["tiny", "480p", "packed", "1344x768", "ref2va"]
+CONFIG_ORDER = ["tiny", "480p", "packed", "1344x768", "ref2va", "long300", "refiner"]
 
 # Seed offset for the second (robustness) seed of each workload.
 ROBUSTNESS_SEED_OFFSET = 1000
@@ -114,6 +165,8 @@ ROBUSTNESS_SEED_OFFSET = 1000
 def item_rows(item: dict) -> int:
     if item["kind"] == "visual":
         return item["T"] * item["H"] * item["W"]
+    if item["kind"] == "clock":
+        return 0
     return item["n"]
 
 

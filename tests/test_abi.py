@@ -65,6 +65,9 @@ def test_layout_edge_cases_bit_exact(L):
         [wl.visual(2, 3, 5), wl.audio(7, 2, attached=True), wl.audio(5, 1.5, attached=False, rule="round"),
          wl.audio(0, 3, attached=False), wl.visual(1, 2, 2), wl.audio(3, 1, attached=True, rule="round")],
         [wl.audio(9, 2.25, attached=False)],
+        [wl.text(4), wl.clock(2.5), wl.visual(1, 2, 2), wl.clock(0.0), wl.audio(3, 1, attached=True),
+         wl.clock(1e6 + 0.25), wl.visual(2, 1, 1), wl.text(0), wl.audio(2, 0.5, attached=False)],
+        [wl.clock(3.0)],
     ]
     cu, pos = H.h3attn_build_layout(segs)
     cu_o, pos_o = oracle.layout(segs)
@@ -93,6 +96,10 @@ def _layout_status(L, items, counts):
         ([_item(1, n=4, span=-1.0)], [1]),
         ([_item(1, n=4, span=1.0, attached=1)], [1]),            # attached audio without a video
         ([_item(1, n=4, span=1.0, rule=7)], [1]),
+        ([_item(2, span=float("nan"))], [1]),                    # clock advance not finite
+        ([_item(2, span=float("inf"))], [1]),
+        ([_item(2, span=-0.5)], [1]),                            # clock going back
+        ([_item(3, n=-1)], [1]),                                 # negative text rows
         ([_item(5)], [1]),                                       # unknown kind
         ([_item(0)], [-1]),
         ([_item(0, T=2048, Hh=2048, W=1024)], [1]),              # more than INT32_MAX tokens

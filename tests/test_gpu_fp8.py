@@ -52,7 +52,7 @@ def test_fp8_peaky_softmax_full(gpu):
     _full(c, "peaky", exact_bars=False)
 
 
-@pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va"])
+@pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va", "long300"])
 @pytest.mark.parametrize("seed_offset", [0, wl.ROBUSTNESS_SEED_OFFSET])
 def test_fp8_workload_sampled_rows(gpu, name, seed_offset):
     cfg = wl.config(name)
@@ -155,6 +155,13 @@ def test_fp8_many_heads_full(gpu):
     c = Case([[wl.visual(2, 16, 16)]], 128, seed=173)
     say(f"fp8 128 heads: N={c.N} H=128")
     _full(c, "128 heads")
+
+
+def test_fp8_refiner_full(gpu):
+    cfg = wl.config("refiner")
+    c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
+    say(f"fp8 refiner: N={c.N} H={c.heads}")
+    _full(c, "refiner")
 
 
 # ---- Skip-Softmax ------------------------------------------------------------------------------

@@ -58,7 +58,7 @@ def _bf16_ulp(v):
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
-@pytest.mark.parametrize("name", ["tiny", "480p", "packed", "ref2va"])
+@pytest.mark.parametrize("name", ["tiny", "480p", "packed", "ref2va", "long300"])
 def test_rope_apply_parity(gpu, name):
     cfg = wl.config(name)
     c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
@@ -117,7 +117,7 @@ def test_peaky_softmax_full(gpu):
             label="peaky")
 
 
-@pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va"])
+@pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va", "long300"])
 @pytest.mark.parametrize("seed_offset", [0, wl.ROBUSTNESS_SEED_OFFSET])
 def test_workload_sampled_rows(gpu, name, seed_offset):
     cfg = wl.config(name)
@@ -272,3 +272,16 @@ def test_many_heads_full(gpu):
     out, lse = c.run()
     o_ref, l_ref = c.oracle_full()
     compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label="128 heads")
+
+
+@pytest.mark.parametrize("seed_offset", [0, wl.ROBUSTNESS_SEED_OFFSET])
+def test_refiner_full(gpu, seed_offset):
+    # the token refiner's short path: eight co-batched prompts (77..645 rows), 56 heads, every
+    # position 0; every row of every head against the oracle
+    cfg = wl.config("refiner")
+    seed = cfg["seed"] + seed_offset
+    c = Case(cfg["segments"], cfg["heads"], seed)
+    say(f"varlen refiner seed {seed}: N={c.N} H={c.heads} lens={c.lens.tolist()}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label=f"refiner/{seed}")

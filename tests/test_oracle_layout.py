@@ -125,3 +125,49 @@ def test_empty_and_degenerate_segments():
 def test_attached_audio_needs_visual():
     with pytest.raises(ValueError):
         oracle.layout([[wl.audio(4, 1, attached=True)]])
+
+
+def test_native_frame_grid_matches_recipe_example():
+    # vLLM-Omni "MiniMax-H3" recipe, "Long video and driving audio": a 75-second request becomes
+    # 1,807 frames (75.292 s at 24 FPS) on the 17n+5 grid
+    assert wl.native_frames(75) == 1807 and abs(1807 / 24 - 75.292) < 5e-4
+    assert wl.latent_frames(1807) == 5 * 106 + 2
+    assert wl.native_frames(300) == 7213 and wl.latent_frames(7213) == 2122
+
+
+def test_long_video_chunk_keeps_global_time():
+    g = _golden("layout_closed_forms.json")["long300"]
+    cu, pos = oracle.layout(wl.config("long300")["segments"])
+    assert cu.tolist() == g["cu_seqlens"]
+    a, b = g["image_rows"], g["image_rows"] + g["chunk_rows"]
+    np.testing.assert_array_equal(pos[:a].astype(np.float64), _grid_positions(1, 24, 42, 0))
+    np.testing.assert_array_equal(pos[a:b].astype(np.float64), _grid_positions(17, 24, 42, g["chunk_t_first"]))
+    assert pos[b - 1, 0] == g["chunk_t_last"]
+    np.testing.assert_array_equal(pos[b:, 0], (g["chunk_t_first"] + np.arange(g["audio_rows"]) / 32.0).astype(np.float32))
+    assert np.all(pos[b:, 1:] == 0)
+
+
+def test_clock_item_moves_only_what_follows():
+    base = [wl.visual(2, 2, 3), wl.audio(4, 2, attached=True), wl.visual(1, 2, 2)]
+    moved = [wl.visual(2, 2, 3), wl.clock(7.5), wl.audio(4, 2, attached=True), wl.visual(1, 2, 2)]
+    _, p0 = oracle.layout([base])
+    _, p1 = oracle.layout([moved])
+    np.testing.assert_array_equal(p0[:16], p1[:16])           # the video and its soundtrack stay
+    np.testing.assert_array_equal(p1[16:, 0], p0[16:, 0] + 7.5)  # the next item starts 7.5 later
+    np.testing.assert_array_equal(p1[16:, 1:], p0[16:, 1:])
+    # a zero advance changes nothing, and advances add up
+    _, pz = oracle.layout([[wl.clock(0.0)] + base])
+    np.testing.assert_array_equal(pz, p0)
+    _, pa = oracle.layout([[wl.clock(3.0), wl.clock(4.5)] + base])
+    _, pb = oracle.layout([[wl.clock(7.5)] + base])
+    np.testing.assert_array_equal(pa, pb)
+
+
+def test_text_rows_sit_at_origin():
+    g = _golden("layout_closed_forms.json")["refiner"]
+    cu, pos = oracle.layout(wl.config("refiner")["segments"])
+    assert cu.tolist() == g["cu_seqlens"]
+    assert np.all(pos == 0)
+    # text rows leave the clock alone
+    _, p = oracle.layout([[wl.text(5), wl.visual(1, 1, 2), wl.text(3), wl.visual(1, 1, 1)]])
+    assert p[5:7, 0].tolist() == [0.0, 0.0] and p[10, 0] == 1.0 and np.all(p[7:10] == 0)
