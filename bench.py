@@ -45,17 +45,24 @@ SKIP_AMPLITUDE = 20.0      # q/k amplitude of the local-attention inputs the ski
 HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
-    "source_sha256": "7d3078f57dc85f252d8222f68aaa3eb9ca3f35a57b184fcf849b16fd00a78f7c",
-    "fetch_kib": 9252052, "fetch_scale": 2.0,
-    "write_kib": 165104, "write_scale": 1.0,
+    "source_sha256": "0c487adeb56bdb9773d694371ab1758c60cd43eec2ae873d8801a9902852b880",
+    "fetch_kib": 3642861, "fetch_scale": 2.0,
+    "write_kib": 165119, "write_scale": 1.0,
+}
+# The same for attn_fwd_fp8_kernel (dense instance, N(0, 1) inputs).
+FP8_HBM_COUNTERS = {
+    "workload": "1344x768",
+    "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_fp8.hip"),
+    "source_sha256": "5358167275d34434a250deded36447d5efece1714677af131c32b690941bc262",
+    "fetch_kib": 1845534, "fetch_scale": 2.0,
+    "write_kib": 190801, "write_scale": 1.0,
 }
 
 
-def counted_traffic(workload):
+def counted_traffic(workload, c=HBM_COUNTERS):
     """Calibrated HBM bytes per attention launch, or None when the counters do not apply."""
     import hashlib
 
-    c = HBM_COUNTERS
     if workload != c["workload"]:
         return None
     try:
@@ -305,6 +312,7 @@ def main():
            "ms_per_step": round(fp8_ms_per_step, 4), "dtype": "fp8 e4m3 operands, fp32 accumulate",
            "roofline": {"bound": "mfma", "achieved": round(fp8_achieved, 2), "peak": PEAK_FP8_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(fp8_achieved / PEAK_FP8_TFLOPS, 4),
+                        "traffic": counted_traffic(name, FP8_HBM_COUNTERS),
                         "kernel": "attn_fwd_fp8_kernel", "kernel_ms": round(fp8_attn_ms, 4)}}
 
     # Skip-Softmax (FP8 mode, threshold 0.05 as in the recipe) on inputs whose attention is local:
