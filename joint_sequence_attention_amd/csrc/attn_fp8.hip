@@ -206,7 +206,11 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
 // bf16 kernel, here with the probabilities stored as p * 2^4: the running
 // value mm is the maximum minus 4, a tile's probabilities stay at most
 // 2^4 after a move and are rescaled once a lane's row sum for a tile
-// exceeds 256, so every stored probability is below 448.
+// exceeds 256, so every stored probability is below 448.  The queries carry
+// the base-2 logit coefficient (scale * log2 e) into their quantization and
+// their power-of-two row scale rides on the matrix core's B scale, so a
+// score MFMA yields base-2 logits; its accumulator starts at -mm, so a
+// probability is one exp2 of the accumulator (no multiply-add per element).
 //
 // LDS: rings of eight key slots and eight value slots of 8 KiB.  Iteration t
 // reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+5) and
@@ -279,12 +283,13 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   load_v(min(2, last_t), ic<2>());
 
   // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 and, for
-  // half ks, dims 64 ks + 32 g .. + 31, rotated in fp32, scaled by the row's
-  // power-of-two factor and rounded to e4m3; cq folds the factor into the
-  // base-2 logit coefficient.
+  // half ks, dims 64 ks + 32 g .. + 31, rotated in fp32 and multiplied by
+  // the base-2 logit coefficient, then scaled by the row's power-of-two
+  // factor and rounded to e4m3; qsc is that factor's 8-bit exponent scale,
+  // which the score MFMAs apply.
   const int qrow = qt * F8_BQ + wave * 32 + l32;
   i32x8 qf[2];
-  float cq;
+  unsigned qsc;
   {
     float f[2][4][8];
     if (qrow < S) {
@@ -298,6 +303,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           const int c = 8 * ks + 4 * g + j;
           unpack8(qp[c], f[ks][j]);
           rope8(f[ks][j], c * 4, s_omega, s_axis, pt, ph, pw);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[ks][j][e] *= scale_log2;
         }
     } else {
 #pragma unroll
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     amax = pair_max(amax);  // the row's other 64 dims sit in lane L ^ 32
     const int eq = e4m3_scale_exponent(amax);
     const float down = ldexpf(1.0f, -eq);
-    cq = scale_log2 * ldexpf(1.0f, eq);
+    qsc = unsigned(eq + E8M0_ONE);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -346,6 +353,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mm = -INFINITY, l = 0.0f;
+  float moff = 0.0f;           // score accumulators start at -moff: 0 until mm is finite, then mm
   float mt = -INFINITY;        // Skip-Softmax: largest base-2 logit of the tiles seen so far
   unsigned n_seen = 0, n_skipped = 0;
   bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
@@ -369,7 +377,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto mfma_qk = [&](f32x16 acc, i32x8 kf, int ks, unsigned ksc) __attribute__((always_inline)) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 0, int(ksc), 0, E8M0_ONE);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 0, int(ksc), 0, int(qsc));
   };
   auto mfma_pv = [&](f32x16 acc, i32x8 vf, const i32x8& p, unsigned vsc) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, p, acc, 0, 0, 0, int(vsc), 0, E8M0_ONE);
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     for (int u = 0; u < 2; ++u) {
       f32x16 acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[r] = -moff;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) acc = mfma_qk(acc, kfrag(SLOT, u, ks), ks, u ? k1 : k0);
       sc[b][u] = acc;
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     constexpr int b = decltype(B)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cq, -mm));
+      p[i] = __builtin_amdgcn_exp2f(sc[b][j >> 2][4 * (j & 3) + i]);
       pin(p[i]);
     }
   };
@@ -436,21 +444,25 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     rs = r;
   };
   // After the exponentials of tile t (buffer B): the rare path that moves the
-  // running maximum (rescaling O and l and recomputing the tile's
-  // probabilities), then the row sum.
-  auto settle = [&](auto B, i32x8& pw, float rs) __attribute__((always_inline)) {
+  // running maximum (rescaling O and l, recomputing the tile's probabilities
+  // and, when the scores of tile t+1 are already under way (PENDING), moving
+  // them to the new start), then the row sum.  The first tile always takes
+  // it: mm is still -inf there.
+  auto settle = [&](auto B, auto PENDING, i32x8& pw, float rs) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
-    const bool over = !(rs <= LAZY_SUM);  // also true for inf and NaN
+    const bool over = !(rs <= LAZY_SUM) || mm == -INFINITY;  // also true for inf and NaN
     if (__builtin_amdgcn_ballot_w64(over) != 0) {
       float mx = sc[b][0][0];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
-      const float tmax = pair_max(mx) * cq;
+      const float tmax = pair_max(mx) + moff;
       const float m_new = fmaxf(mm, tmax - P_SHIFT);
       const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf
+      const float shift = moff - m_new;
       mm = m_new;
+      moff = m_new;
       l *= a;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -461,9 +473,15 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       for (int j = 0; j < 8; ++j) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cq, -mm));
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[b][j >> 2][4 * (j & 3) + i] + shift);
         pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
         rs += (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      if constexpr (decltype(PENDING)::value != 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[1 - b][u][r] += shift;
       }
     }
     l += rs;
@@ -499,8 +517,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         const int u = j & 1, ks = j >> 1;
         f32x16 acc;
         if (ks == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+          acc = splat16(-moff);  // the first half starts the chain at -moff
         } else {
           acc = sc[1 - b][u];
         }
@@ -532,7 +549,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     if (do_exp) {
-      settle(ic<b>(), pw, rs);
+      settle(ic<b>(), QK, pw, rs);
       pf[b] = pw;
     }
   };
@@ -548,7 +565,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
-    const float tm = pair_max(mx) * cq;
+    const float tm = pair_max(mx) + moff;
     const bool lets_go = qrow >= S || tm < mt + skip_log2;
     mt = fmaxf(mt, tm);
     return __builtin_amdgcn_ballot_w64(!lets_go) == 0;

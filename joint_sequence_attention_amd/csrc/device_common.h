@@ -68,6 +68,17 @@ __device__ __forceinline__ int e4m3_scale_exponent(float amax) {
   return max(-127, min(127, e));
 }
 
+// Sixteen copies of x, built from 64-bit halves so that the compiler can
+// materialize them with 64-bit moves.
+__device__ __forceinline__ f32x16 splat16(float x) {
+  typedef __attribute__((__vector_size__(8 * sizeof(unsigned long long)))) unsigned long long u64x8;
+  const unsigned long long w = (unsigned long long)__float_as_uint(x) * 0x100000001ull;
+  u64x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = w;
+  return __builtin_bit_cast(f32x16, z);
+}
+
 // Max / sum with the partner lane (L ^ 32).
 __device__ __forceinline__ float pair_max(float x) {
   const unsigned u = __float_as_uint(x);

@@ -27,8 +27,13 @@ The steps, in that order, with the readings taken where the page is silent:
    from the segment start, all 128 dims (reading: the page says V is FP8 but
    gives no V block size).  Each element is x8 = e4m3(x * 2**-e), rounded to
    nearest even, and stands for x8 * 2**e.
-4. z = q8 k8^T * scale, exact softmax per row: m = max z, p = exp(z - m),
-   l = sum p, lse = m + ln l.
+4. The softmax scale enters through the queries: each rotated query row is
+   multiplied by c = scale * log2(e) and held in float32 before it is
+   quantized, so q8 k8^T is the row's logits in base 2; z = (q8 k8^T) ln 2.
+   Reading: the page does not say where the scale enters; putting it into Q
+   before quantization gives a kernel base-2 logits straight from the matrix
+   core.  Exact softmax per row: m = max z, p = exp(z - m), l = sum p,
+   lse = m + ln l.
 5. P in FP8 (``quantize_p``): p8 = e4m3(p * 16) / 16, i.e. probabilities
    relative to the row maximum, scaled by 2**4 so that values down to 2**-10
    stay normal (reading: the page gives no P scale).  out = (p8 v8) / l.
@@ -80,6 +85,7 @@ V_BLOCK = 64                       # keys per scale (all dims)
 P_SCALE_LOG2 = 4                   # P is quantized as p * 2**4
 SKIP_QUERY_BLOCK = 32              # Skip-Softmax: query rows that decide together
 SKIP_KEY_TILE = 64                 # Skip-Softmax: keys skipped together
+LN2 = math.log(2.0)
 
 
 def round_e4m3(x) -> np.ndarray:
@@ -323,6 +329,7 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    c = scale / LN2                     # base-2 logit coefficient, folded into the queries
     seg_of = np.searchsorted(cu, rows, side="right") - 1
     out = np.zeros((len(rows), len(heads), D), dtype=np.float64)
     lse = np.zeros((len(heads), len(rows)), dtype=np.float64)
@@ -349,8 +356,9 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
         else:
             ev = want
         q_rows = np.asarray(q[a + ev][:, heads, :], dtype=np.float64)
-        qr = _to_f32(rope(q_rows, pos[a + ev], theta, dims))
-        qw = 2.0 * rotation_error_bound(q_rows, pos[a + ev], theta, dims)
+        qr = _to_f32(_to_f32(rope(q_rows, pos[a + ev], theta, dims)) * c)
+        # the rotation window times c, plus the float32 roundings of c and of the product
+        qw = 2.0 * rotation_error_bound(q_rows, pos[a + ev], theta, dims) * abs(c) + np.abs(qr) * 2.0 ** -22
         qq = np.empty_like(qr)
         qc = np.empty_like(qr)
         for i in range(qr.shape[0]):
@@ -367,9 +375,9 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
                 keep = amb = None
                 if skip_threshold:
                     qp, qcp = qq[part, j, :], qc[part, j, :]
-                    z = (qp @ kq[:, j, :].T) * scale
-                    za = (np.abs(qp) @ np.abs(kq[:, j, :]).T).max(axis=1) * abs(scale)
-                    dzmax = ((np.abs(qp) @ kc[:, j, :].T + qcp @ np.abs(kq[:, j, :]).T) * abs(scale)).max(axis=1)
+                    z = (qp @ kq[:, j, :].T) * LN2
+                    za = (np.abs(qp) @ np.abs(kq[:, j, :]).T).max(axis=1) * LN2
+                    dzmax = ((np.abs(qp) @ kc[:, j, :].T + qcp @ np.abs(kq[:, j, :]).T) * LN2).max(axis=1)
                     delta = 2.0 ** -14 * za + dzmax
                     evp = ev[part]
                     keep = np.ones((len(evp), S_seg), dtype=bool)
@@ -383,7 +391,7 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
                         amb[in_b] = am
                     del z
                 o, l, (sg, za2, lf, of) = _segment_head(
-                    qq[part, j, :], kq[:, j, :], vq[:, j, :], scale, quantize_p, qc[part, j, :], kc[:, j, :], keep,
+                    qq[part, j, :], kq[:, j, :], vq[:, j, :], LN2, quantize_p, qc[part, j, :], kc[:, j, :], keep,
                     amb, SKIP_KEY_TILE)
                 idx = np.arange(len(ev))[part]
                 sel_here = np.nonzero(np.isin(pick, idx))[0]

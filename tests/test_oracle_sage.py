@@ -105,18 +105,27 @@ def test_key_blocks_start_at_row_zero_and_are_independent():
     assert np.array_equal(got[32:], sage.quantize_block(x[32:]))        # the short last block stands alone
 
 
+C_DEFAULT = 1.0 / math.sqrt(D) / math.log(2.0)     # the base-2 logit coefficient at the default scale
+
+
 def _exact_inputs(n, h, seed):
-    """Inputs that the block quantization leaves unchanged: e4m3 values whose every block holds 448."""
+    """Inputs that the block quantization leaves unchanged.
+
+    k and v: e4m3 values whose every block holds 448.  q: e4m3 values / c, so that the scaled
+    rows c q that get quantized are e4m3 values again (up to float32 rounding, which rounds back
+    to them); each row holds 416, clear of the 448 boundary where such a rounding could move the
+    row's scale.
+    """
     rng = np.random.default_rng(seed)
     g = _e4m3_grid()
-    pick = lambda shape: g[rng.integers(0, 127, shape)] * rng.choice([-1.0, 1.0], shape)
-    q, k, v = pick((n, h, D)), pick((n, h, D)), pick((n, h, D))
-    q[:, :, 0] = 448.0
+    pick = lambda shape, top: g[rng.integers(0, top, shape)] * rng.choice([-1.0, 1.0], shape)
+    q, k, v = pick((n, h, D), 126), pick((n, h, D), 127), pick((n, h, D), 127)   # code 125 is 416
+    q[:, :, 0] = 416.0
     for r0 in range(0, n, 16):
         k[r0, :, 0] = 448.0
     for r0 in range(0, n, 64):
         v[r0, :, 0] = 448.0
-    return q / 64.0, k / 64.0, v            # scales 2^-6: the block maxima become 7, still exact
+    return q / 64.0 / C_DEFAULT, k / 64.0, v     # scales 2^-6: still exact
 
 
 def test_sage_equals_exact_attention_when_quantization_is_exact():
@@ -158,6 +167,12 @@ def test_sage_p_rounding_stays_within_its_bound():
     assert np.sqrt(np.mean(ratio ** 2)) < 1.0 and ratio.max() < 6.0
 
 
+def _scaled_query(x, scale):
+    """The row that gets quantized: float32(float32(x) * scale * log2 e), element by element."""
+    c = scale / math.log(2.0)
+    return np.array([float(np.float32(float(np.float32(t)) * c)) for t in x.ravel()]).reshape(x.shape)
+
+
 def _brute_sage(q, k, v, cu, scale):
     """Loops over segment, head and query row; quantization from the block definition, written out."""
     N, H, _ = q.shape
@@ -181,8 +196,8 @@ def _brute_sage(q, k, v, cu, scale):
             kq = np.concatenate([qblock(k[j:min(j + 16, b), h]) for j in range(a, b, 16)])
             vq = np.concatenate([qblock(v[j:min(j + 64, b), h]) for j in range(a, b, 64)])
             for i in range(a, b):
-                qq = qblock(q[i, h])
-                z = [sum(qq[d] * kq[j][d] for d in range(D)) * scale for j in range(b - a)]
+                qq = qblock(_scaled_query(q[i, h], scale))           # base-2 logits come out of q8 k8
+                z = [sum(qq[d] * kq[j][d] for d in range(D)) * math.log(2.0) for j in range(b - a)]
                 zm = max(z)
                 p = [math.exp(t - zm) for t in z]
                 tot = sum(p)
@@ -385,10 +400,10 @@ def test_skip_matches_brute_force():
     q, k, v, pos, cu = _skip_case(22, n=230, qscale=3.0)
     out, lse, es = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, skip_threshold=0.05, error_scales=True)
     # the same quantized operands, through the brute-force rule
-    q8 = sage.quantize_rows(q[:, 0])
+    q8 = sage.quantize_rows(_scaled_query(q[:, 0], 1.0 / math.sqrt(D)))
     k8 = sage.quantize_key_blocks(k[:, 0], 16)
     v8 = sage.quantize_key_blocks(v[:, 0], 64)
-    bo, bl, keep = _brute_skip(q8, k8, v8, 1.0 / math.sqrt(D), 0.05)
+    bo, bl, keep = _brute_skip(q8, k8, v8, math.log(2.0), 0.05)
     assert np.max(np.abs(out[:, 0] - bo)) <= 1e-12 and np.max(np.abs(lse[0] - bl)) <= 1e-12
     share = 1.0 - np.array([sum(keep[i][::64]) for i in range(len(keep))]) / 4.0
     assert np.allclose(es["skipped"][0], share)
