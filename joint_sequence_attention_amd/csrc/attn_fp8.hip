@@ -353,7 +353,12 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mm = -INFINITY, l = 0.0f;
-  float moff = 0.0f;           // score accumulators start at -moff: 0 until mm is finite, then mm
+  // Dense instance: score accumulators start at -moff (0 until mm is finite,
+  // then mm), so the exponentials need no subtraction.  The Skip-Softmax
+  // instance starts them at 0 and subtracts mm in the exponent: the start
+  // tuple's sixteen registers would push its loop into scratch reloads.
+  constexpr bool START_AT_M = !SKIP;
+  float moff = 0.0f;
   float mt = -INFINITY;        // Skip-Softmax: largest base-2 logit of the tiles seen so far
   unsigned n_seen = 0, n_skipped = 0;
   bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
@@ -397,7 +402,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     for (int u = 0; u < 2; ++u) {
       f32x16 acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = -moff;
+      for (int r = 0; r < 16; ++r) acc[r] = START_AT_M ? -moff : 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) acc = mfma_qk(acc, kfrag(SLOT, u, ks), ks, u ? k1 : k0);
       sc[b][u] = acc;
@@ -429,7 +434,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     constexpr int b = decltype(B)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(sc[b][j >> 2][4 * (j & 3) + i]);
+      const float x = sc[b][j >> 2][4 * (j & 3) + i];
+      p[i] = __builtin_amdgcn_exp2f(START_AT_M ? x : x - mm);
       pin(p[i]);
     }
   };
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf
       const float shift = moff - m_new;
       mm = m_new;
-      moff = m_new;
+      if constexpr (START_AT_M) moff = m_new;
       l *= a;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
         rs += (p[0] + p[1]) + (p[2] + p[3]);
       }
-      if constexpr (decltype(PENDING)::value != 0) {
+      if constexpr (START_AT_M && decltype(PENDING)::value != 0) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -517,7 +523,12 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         const int u = j & 1, ks = j >> 1;
         f32x16 acc;
         if (ks == 0) {
-          acc = splat16(-moff);  // the first half starts the chain at -moff
+          if constexpr (START_AT_M) {
+            acc = splat16(-moff);  // the first half starts the chain at -moff
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+          }
         } else {
           acc = sc[1 - b][u];
         }
