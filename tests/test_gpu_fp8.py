@@ -243,3 +243,45 @@ def test_fp8_skip_workload_sampled_rows(gpu):
     rows = c.sample_rows(n_random=16, seed=183)
     say(f"fp8 skip 1344x768: N={c.N} H={c.heads}, {len(rows)} rows (whole 32-row blocks evaluated)")
     _skip_run(c, 0.05, rows=rows, label="skip 1344x768")
+
+
+# ---- Running maximum that moves on every tile ----------------------------------------------------
+
+
+def _rising_case(n_tokens, heads, seed, top=40.0):
+    """Keys that line up with the queries and grow along the sequence: every 64-key tile holds
+    larger logits than the one before, so the running maximum moves on every tile (up to ~top
+    natural units), with ragged segment lengths."""
+    from helpers import bits_to_device
+    rng = np.random.default_rng(seed)
+    c = rng.standard_normal((heads, 128))
+    c /= np.linalg.norm(c, axis=1, keepdims=True)
+    ramp = np.linspace(0.0, 1.0, n_tokens)[:, None, None]
+    q = 3.0 * c[None] + 0.3 * rng.standard_normal((n_tokens, heads, 128))
+    k = (top * np.sqrt(128) / 3.0) * ramp * c[None] + 0.3 * rng.standard_normal((n_tokens, heads, 128))
+    v = rng.standard_normal((n_tokens, heads, 128))
+
+    def bits(x):
+        return wl._round_bf16_bits(np.ascontiguousarray(x, dtype=np.float32))
+    lens = [1, 63, 64, 65, 200, n_tokens - 393]
+    c0 = Case([[wl.visual(1, 1, n)] for n in lens], heads, seed)
+    c0.qb, c0.kb, c0.vb = bits(q), bits(k), bits(v)
+    dev = c0.q.device
+    c0.q, c0.k, c0.v = bits_to_device(c0.qb, dev), bits_to_device(c0.kb, dev), bits_to_device(c0.vb, dev)
+    return c0
+
+
+def test_fp8_running_maximum_moves_every_tile(gpu):
+    c = _rising_case(1200, 2, 190)
+    say(f"fp8 rising logits: lens={c.lens.tolist()}")
+    _full(c, "rising", exact_bars=False)
+
+
+def test_fp8_very_large_logits(gpu):
+    # q x 64: logits of several hundred, far past exp2's range without a reference; every row
+    # must still come out finite and match the oracle
+    c = Case(ragged_segments(), 2, 191, qscale=64.0)
+    say(f"fp8 very large logits: lens={c.lens.tolist()}")
+    out, lse = c.run_fp8()
+    assert np.all(np.isfinite(device_to_f64(out))) and np.all(np.isfinite(device_to_f64(lse)))
+    _full(c, "large logits", exact_bars=False)

@@ -285,3 +285,30 @@ def test_refiner_full(gpu, seed_offset):
     out, lse = c.run()
     o_ref, l_ref = c.oracle_full()
     compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, label=f"refiner/{seed}")
+
+
+def test_running_maximum_moves_every_tile(gpu):
+    # Every tile holds larger logits than the one before (the lazy rescale runs on every tile),
+    # up to ~50 at the end of the long segment.  There the score operands' 11 significant bits
+    # move lse beyond the N(0, 1) bar: rounding this very case's rotated operands to 11 bits
+    # (float64 otherwise) moves lse by up to 2.7e-3 and out by up to 1.9e-3.  lse bar at about
+    # four times that; out keeps the default bar.
+    from test_gpu_fp8 import _rising_case
+    c = _rising_case(1200, 2, 192)
+    say(f"varlen rising logits: lens={c.lens.tolist()}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, lse_max=1e-2, label="rising")
+
+
+def test_very_large_logits(gpu):
+    # q x 64: logits up to ~320.  The score operands carry 11 significant bits, so a logit moves
+    # by up to ~|z| 2^-11 times the spread of its products; rounding the rotated operands of this
+    # very case to 11 bits (float64 otherwise) moves out by up to 0.048 (mean 4.4e-4) and lse by
+    # up to 0.066.  Bars at about four times that.
+    c = Case(ragged_segments(), 2, 193, qscale=64.0)
+    say(f"varlen very large logits: lens={c.lens.tolist()}")
+    out, lse = c.run()
+    o_ref, l_ref = c.oracle_full()
+    compare(device_to_f64(out), device_to_f64(lse), o_ref, l_ref, out_max=0.2, out_mean=5e-3, lse_max=0.2,
+            label="large logits")
