@@ -170,8 +170,19 @@ def survey_workload(name, steps, warmup):
                                                          workspace=ws8))
     H.h3attn_varlen_kv_prologue_fp8(k, v, cu_d, pos_d, max_seqlen, ws8)
     fp8_attn_ms = timed(lambda: H.h3attn_varlen_attention_fp8(q, cu_d, pos_d, max_seqlen, ws8, out=out, lse=lse))
+    # The whole step captured once in a HIP graph and replayed: what a caller that replays its
+    # launches saves on launch overhead (it matters for the short workloads).
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            H.h3attn_varlen_fwd(q, k, v, cu_d, pos_d, max_seqlen, out=out, lse=lse, workspace=ws,
+                                stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph_step_ms = timed(graph.replay)
     return {"workload": name, "tokens": N, "heads": heads, "segments": int(len(lens)), "flop": flop,
             "step_ms": round(step_ms, 4), "step_tflops": round(flop / step_ms / 1e9, 1),
+            "graph_step_ms": round(graph_step_ms, 4),
             "attn_ms": round(attn_ms, 4), "attn_tflops": round(flop / attn_ms / 1e9, 1),
             "attn_pct_of_peak": round(100 * flop / attn_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "rope_apply_ms": round(rope_ms, 4), "rope_apply_gbps": round(rope_bytes / rope_ms / 1e6, 1),
