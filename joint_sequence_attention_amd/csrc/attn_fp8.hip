@@ -501,7 +501,11 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // share the probabilities).  Exponential unit j of tile t follows slot j,
   // then tile t settles.  Two fragment registers alternate, each read one or
   // two slots ahead of its MFMA (the first two at the start).  A scheduling
-  // fence after every slot keeps this order.
+  // fence after every slot keeps this order.  The Skip-Softmax instance keeps
+  // the MFMA order but groups the exponentials: units 0..3 after the score
+  // MFMAs and units 4..7 after the value MFMAs, each group under one
+  // wave-uniform branch, the value MFMAs under a third (a left-out tile then
+  // skips three branches, where interleaving needed twelve).
   auto region = [&](auto B, auto QK, auto PV, bool do_exp, bool pv_live, auto kslot, auto vslot, unsigned k0,
                     unsigned k1, unsigned vsc) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
@@ -517,47 +521,98 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       fr[0] = vfrag(vslot, 0);
       fr[1] = vfrag(vslot, 1);
     }
+    if constexpr (SKIP) {
+      // Skip-Softmax instance: the MFMAs of each half, then its exponentials
+      // under one wave-uniform branch.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (do_qk) {
-        const int u = j & 1, ks = j >> 1;
-        f32x16 acc;
-        if (ks == 0) {
-          if constexpr (START_AT_M) {
-            acc = splat16(-moff);  // the first half starts the chain at -moff
-          } else {
+      for (int j = 0; j < 4; ++j) {
+        if (do_qk) {
+          const int u = j & 1, ks = j >> 1;
+          f32x16 acc;
+          if (ks == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+          } else {
+            acc = sc[1 - b][u];
           }
-        } else {
-          acc = sc[1 - b][u];
+          sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u ? k1 : k0);
+          if (j < 2)
+            fr[u] = kfrag(kslot, u, 1);
+          else if (do_pv)
+            fr[u] = vfrag(vslot, j - 2);
         }
-        sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u ? k1 : k0);
-        // next fragment into the register this MFMA has read
-        if (j < 2)
-          fr[u] = kfrag(kslot, u, 1);
-        else if (do_pv)
-          fr[u] = vfrag(vslot, j - 2);
-      }
-      if (do_exp) {
-        float p[4];
-        exp_unit(ic<b>(), j, p);
-        pack_unit(j, p, pw, rs);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+      if (do_exp) {
 #pragma unroll
-    for (int j = 4; j < 8; ++j) {
-      if (do_pv) {
-        if (pv_live) o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
-        if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
-      }
-      if (do_exp) {
-        float p[4];
-        exp_unit(ic<b>(), j, p);
-        pack_unit(j, p, pw, rs);
+        for (int j = 0; j < 4; ++j) {
+          float p[4];
+          exp_unit(ic<b>(), j, p);
+          pack_unit(j, p, pw, rs);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (do_pv) {
+        if (pv_live) {
+#pragma unroll
+          for (int j = 4; j < 8; ++j) {
+            o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
+            if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_exp) {
+#pragma unroll
+        for (int j = 4; j < 8; ++j) {
+          float p[4];
+          exp_unit(ic<b>(), j, p);
+          pack_unit(j, p, pw, rs);
+        }
+      }
+    } else {
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (do_qk) {
+          const int u = j & 1, ks = j >> 1;
+          f32x16 acc;
+          if (ks == 0) {
+            if constexpr (START_AT_M) {
+              acc = splat16(-moff);  // the first half starts the chain at -moff
+            } else {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            }
+          } else {
+            acc = sc[1 - b][u];
+          }
+          sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u ? k1 : k0);
+          // next fragment into the register this MFMA has read
+          if (j < 2)
+            fr[u] = kfrag(kslot, u, 1);
+          else if (do_pv)
+            fr[u] = vfrag(vslot, j - 2);
+        }
+        if (do_exp) {
+          float p[4];
+          exp_unit(ic<b>(), j, p);
+          pack_unit(j, p, pw, rs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  #pragma unroll
+      for (int j = 4; j < 8; ++j) {
+        if (do_pv) {
+          if (pv_live) o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
+          if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
+        }
+        if (do_exp) {
+          float p[4];
+          exp_unit(ic<b>(), j, p);
+          pack_unit(j, p, pw, rs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (do_exp) {
       settle(ic<b>(), QK, pw, rs);
