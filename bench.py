@@ -53,9 +53,9 @@ HBM_COUNTERS = {
 FP8_HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_fp8.hip"),
-    "source_sha256": "7a13af9316dc58e2f97595266ea974028c1c840db9a438c7d1190419bd5ea2da",
-    "fetch_kib": 2103986, "fetch_scale": 2.0,
-    "write_kib": 297447, "write_scale": 1.0,
+    "source_sha256": "1849dd10cdb0cdb2d8c502b447f4cf806435467639d61d9e406e7a3a0527925f",
+    "fetch_kib": 2088860, "fetch_scale": 2.0,
+    "write_kib": 297224, "write_scale": 1.0,
 }
 
 
