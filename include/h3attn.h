@@ -203,8 +203,9 @@ h3attn_status h3attn_varlen_attention(const void* q, const int32_t* cu_seqlens, 
  * and lse are then softmax over the kept tiles.  Whether to use it for a
  * given denoising step (the recipe keeps the early, high-noise steps dense)
  * is the caller's choice.  skip_stats: NULL, or device uint64[2] to which the
- * call adds the (block, tile) pairs it saw and those it left out; the caller
- * clears it.  Fails with INVALID_ARG for a threshold outside [0, 1).
+ * call adds the (block, tile) pairs it saw and those it left out (nothing
+ * when skip_threshold is 0); the caller clears it.  Fails with INVALID_ARG
+ * for a threshold outside [0, 1).
  * ------------------------------------------------------------------- */
 size_t h3attn_varlen_fwd_fp8_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs);
 
