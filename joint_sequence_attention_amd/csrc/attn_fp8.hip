@@ -296,16 +296,29 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       const int64_t tok = int64_t(seg_a) + qrow;
       const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
       const u32x4* qp = q + (tok * n_heads + h) * CHUNKS_PER_ROW;
+      // The test reads only the positions, so a turning wave computes its
+      // angles while the query chunks are still in flight.
+      if (wave_at_origin(pt, ph, pw)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) unpack8(qp[8 * ks + 4 * g + j], f[ks][j]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = 8 * ks + 4 * g + j;
+            unpack8(qp[c], f[ks][j]);
+            rope_turn4(f[ks][j], rope_angles4(c * 4, s_omega, s_axis, pt, ph, pw));
+          }
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = 8 * ks + 4 * g + j;
-          unpack8(qp[c], f[ks][j]);
-          rope8(f[ks][j], c * 4, s_omega, s_axis, pt, ph, pw);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[ks][j][e] *= scale_log2;
-        }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)

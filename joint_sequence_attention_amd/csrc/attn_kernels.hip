@@ -164,8 +164,23 @@ __device__ __forceinline__ void rope_turn4(float (&x)[8], const Rot4& r) {
   }
 }
 
+// A token at position (0, 0, 0) turns every pair by angle 0, the identity
+// (sin 0 = 0 and cos 0 = 1 are exact), so its rows may be left as they are.
+// The test is taken per wave: when every active lane holds such a token (a
+// wave of text rows) the angles are skipped with one scalar branch; a wave
+// with any other token turns all its lanes, which changes no value of a
+// lane at the origin except the sign of a zero.
+__device__ __forceinline__ bool at_origin(float pt, float ph, float pw) {
+  return pt == 0.0f && ph == 0.0f && pw == 0.0f;
+}
+
+__device__ __forceinline__ bool wave_at_origin(float pt, float ph, float pw) {
+  return __builtin_amdgcn_ballot_w64(!at_origin(pt, ph, pw)) == 0;
+}
+
 __device__ __forceinline__ void rope8(float (&x)[8], int pair0, const float* s_omega, const int* s_axis,
                                       float pt, float ph, float pw) {
+  if (wave_at_origin(pt, ph, pw)) return;
   rope_turn4(x, rope_angles4(pair0, s_omega, s_axis, pt, ph, pw));
 }
 
@@ -192,8 +207,14 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const u32x4* x, u32x4* 
   for (int64_t it = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; it < n_items; it += stride) {
     const int64_t tok = it / CHUNKS_PER_ROW;
     const int c = int(it % CHUNKS_PER_ROW);
-    const Rot4 r = rope_angles4(c * 4, s_omega, s_axis, pos[3 * tok], pos[3 * tok + 1], pos[3 * tok + 2]);
+    const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
     const int64_t base = tok * n_heads * CHUNKS_PER_ROW + c;
+    if (at_origin(pt, ph, pw)) {  // the identity: copy (nothing to do in place)
+      if (x != y)
+        for (int h = 0; h < n_heads; ++h) y[base + int64_t(h) * CHUNKS_PER_ROW] = x[base + int64_t(h) * CHUNKS_PER_ROW];
+      continue;
+    }
+    const Rot4 r = rope_angles4(c * 4, s_omega, s_axis, pt, ph, pw);
     int h = 0;
     for (; h + 4 <= n_heads; h += 4) {  // four loads in flight before any use
       u32x4 v[4];
@@ -466,10 +487,17 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
       const int64_t tok = int64_t(seg_a) + qrow;
       const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
       const u32x4* qp = q + (tok * n_heads + h) * CHUNKS_PER_ROW;
+      // The test reads only the positions, so a turning wave computes its
+      // angles while the query chunks are still in flight.
+      if (wave_at_origin(pt, ph, pw)) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        unpack8(qp[2 * ks + g], f[ks]);
-        rope8(f[ks], ks * 8 + g * 4, s_omega, s_axis, pt, ph, pw);
+        for (int ks = 0; ks < 8; ++ks) unpack8(qp[2 * ks + g], f[ks]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          unpack8(qp[2 * ks + g], f[ks]);
+          rope_turn4(f[ks], rope_angles4(ks * 8 + g * 4, s_omega, s_axis, pt, ph, pw));
+        }
       }
     } else {
 #pragma unroll

@@ -121,8 +121,23 @@ __device__ __forceinline__ void rope_turn4(float (&x)[8], const Rot4& r) {
   }
 }
 
+// A token at position (0, 0, 0) turns every pair by angle 0, the identity
+// (sin 0 = 0 and cos 0 = 1 are exact), so its rows may be left as they are.
+// The test is taken per wave: when every active lane holds such a token (a
+// wave of text rows) the angles are skipped with one scalar branch; a wave
+// with any other token turns all its lanes, which changes no value of a
+// lane at the origin except the sign of a zero.
+__device__ __forceinline__ bool at_origin(float pt, float ph, float pw) {
+  return pt == 0.0f && ph == 0.0f && pw == 0.0f;
+}
+
+__device__ __forceinline__ bool wave_at_origin(float pt, float ph, float pw) {
+  return __builtin_amdgcn_ballot_w64(!at_origin(pt, ph, pw)) == 0;
+}
+
 __device__ __forceinline__ void rope8(float (&x)[8], int pair0, const float* s_omega, const int* s_axis,
                                       float pt, float ph, float pw) {
+  if (wave_at_origin(pt, ph, pw)) return;
   rope_turn4(x, rope_angles4(pair0, s_omega, s_axis, pt, ph, pw));
 }
 
