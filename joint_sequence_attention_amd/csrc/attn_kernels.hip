@@ -209,12 +209,15 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const u32x4* x, u32x4* 
     const int c = int(it % CHUNKS_PER_ROW);
     const float pt = pos[3 * tok], ph = pos[3 * tok + 1], pw = pos[3 * tok + 2];
     const int64_t base = tok * n_heads * CHUNKS_PER_ROW + c;
-    if (at_origin(pt, ph, pw)) {  // the identity: copy (nothing to do in place)
-      if (x != y)
-        for (int h = 0; h < n_heads; ++h) y[base + int64_t(h) * CHUNKS_PER_ROW] = x[base + int64_t(h) * CHUNKS_PER_ROW];
-      continue;
+    // At the origin every angle is +0, whose sine and cosine are exactly +0
+    // and 1: that Rot4 is written out instead of computed, bit for bit the same.
+    Rot4 r;
+    if (at_origin(pt, ph, pw)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.sn[i] = 0.0f, r.cs[i] = 1.0f;
+    } else {
+      r = rope_angles4(c * 4, s_omega, s_axis, pt, ph, pw);
     }
-    const Rot4 r = rope_angles4(c * 4, s_omega, s_axis, pt, ph, pw);
     int h = 0;
     for (; h + 4 <= n_heads; h += 4) {  // four loads in flight before any use
       u32x4 v[4];
