@@ -138,8 +138,9 @@ h3attn_status h3attn_rope_apply(const void* x, void* y, const float* pos_thw, in
  *
  * The workspace (device, >= h3attn_varlen_fwd_workspace_size bytes, 256-byte
  * aligned) holds the rotated keys (fp16, each 64-key tile scaled by a power
- * of two), the transposed values and the per-tile key scales, in the layout
- * the attention kernel reads; its contents on return are unspecified.
+ * of two), the transposed values, the per-tile key scales and the segments'
+ * order by length (the attention grid starts the longest first), in the
+ * layout the attention kernel reads; its contents on return are unspecified.
  *
  * Precision: the rotated queries and keys enter the score contraction as
  * fp16 with power-of-two block scales (one per query row, one per 64-key
@@ -158,10 +159,11 @@ h3attn_status h3attn_varlen_fwd(const void* q, const void* k, const void* v, con
  * h3attn_varlen_attention on the same stream, with the same arguments,
  * computes exactly what h3attn_varlen_fwd computes.
  *
- * kv_prologue: rotates k and packs it, with v transposed, into the workspace.
+ * kv_prologue: rotates k and packs it, with v transposed, into the workspace,
+ *              and ranks the segments by length there.
  * attention:   rotates q as it loads it and runs the attention kernel on the
  *              packed keys and values; it reads k and v only through the
- *              workspace. */
+ *              workspace, and takes its segment order from it. */
 h3attn_status h3attn_varlen_kv_prologue(const void* k, const void* v, const int32_t* cu_seqlens,
                                         const float* pos_thw, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                                         int32_t n_seqs, int32_t max_seqlen, const h3attn_rope_cfg* rope,

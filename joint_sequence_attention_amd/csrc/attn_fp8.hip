@@ -90,11 +90,12 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
                                                               RopeTable tab, u32x2* __restrict__ k_ws,
                                                               unsigned* __restrict__ v_ws,
                                                               unsigned* __restrict__ k_sc, unsigned* __restrict__ v_sc,
-                                                              int64_t rows_per_head) {
+                                                              int32_t* __restrict__ order, int64_t rows_per_head) {
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
   __shared__ float s_red[4][5];
   const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  if (tile == 0 && h == 0) write_segment_rank(cu, int(gridDim.y), s, order);  // before any early exit
   const int32_t seg_a = cu[s];
   const int32_t S = cu[s + 1] - seg_a;
   if (tile * KT >= S) return;  // whole block leaves together
@@ -222,15 +223,17 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const char* __restrict__ k_ws, const char* __restrict__ v_ws,
-    const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_sc, int64_t rows_per_head, float skip_log2,
-    unsigned long long* __restrict__ skip_stats) {
+    const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_sc, const int32_t* __restrict__ order,
+    int64_t rows_per_head, float skip_log2, unsigned long long* __restrict__ skip_stats) {
   static_assert(F8_TILE_BYTES / 16 == F8_NW * 64, "one direct load per lane, tile and tensor");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
 
-  const int qt = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  // The segment comes from the rank order the K/V prologue wrote.
+  const int qt = blockIdx.x, h = blockIdx.y;
+  const int s = gridDim.z == 1 ? 0 : order[blockIdx.z];
   const int32_t seg_a = cu[s];
   const int32_t S = cu[s + 1] - seg_a;
   if (qt * F8_BQ >= S) return;  // whole block leaves together
@@ -779,20 +782,20 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 
 int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, const float* pos, int32_t n_heads,
                            int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws, void* v_ws,
-                           unsigned* k_sc, unsigned* v_sc, int64_t rows_per_head, void* stream) {
+                           unsigned* k_sc, unsigned* v_sc, int32_t* order, int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + KT - 1) / KT);
   if (tiles == 0) return 0;
   hipLaunchKernelGGL(kv_prologue_fp8_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                      cu, pos, n_heads, table, static_cast<u32x2*>(k_ws), static_cast<unsigned*>(v_ws), k_sc, v_sc,
-                     rows_per_head);
+                     order, rows_per_head);
   return int(hipGetLastError());
 }
 
 int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
                          int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
                          float skip_threshold, const RopeTable& table, const void* k_ws, const void* v_ws,
-                         const unsigned* k_sc, const unsigned* v_sc, int64_t rows_per_head,
+                         const unsigned* k_sc, const unsigned* v_sc, const int32_t* order, int64_t rows_per_head,
                          unsigned long long* skip_stats, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + F8_BQ - 1) / F8_BQ);
   if (tiles == 0) return 0;
@@ -812,18 +815,19 @@ int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, voi
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   const float skip_log2 = skip ? std::log2(skip_threshold) : 0.0f;
-  const dim3 grid(tiles, unsigned(n_seqs), unsigned(n_heads));
+  // Grid (query tile, head, segment rank): the longest segments go first.
+  const dim3 grid(tiles, unsigned(n_heads), unsigned(n_seqs));
   if (skip)
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, grid, dim3(F8_NW * 64), F8_SMEM, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(q), cu, pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens),
                        n_heads, scale_log2, table, static_cast<const char*>(k_ws), static_cast<const char*>(v_ws),
-                       k_sc, v_sc, rows_per_head, skip_log2, skip_stats);
+                       k_sc, v_sc, order, rows_per_head, skip_log2, skip_stats);
   else
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, grid, dim3(F8_NW * 64), F8_SMEM,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu, pos,
                        static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
-                       static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_sc, rows_per_head,
-                       0.0f, nullptr);
+                       static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_sc, order,
+                       rows_per_head, 0.0f, nullptr);
   return int(hipGetLastError());
 }
 

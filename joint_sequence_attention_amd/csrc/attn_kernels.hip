@@ -191,6 +191,29 @@ __device__ __forceinline__ void stage_rope_table(const RopeTable& tab, float* s_
   }
 }
 
+// Called by every thread of one workgroup per segment s (a block-uniform
+// condition): writes order[rank] = s, where segments rank by length, longest
+// first, equal lengths by index.  That key is a strict total order, so order
+// becomes a permutation of 0 .. n_seqs-1 whatever cu holds.  The attention
+// grid walks it so that the longest segments' workgroups start first and the
+// grid ends on short ones.
+__device__ __forceinline__ void write_segment_rank(const int32_t* cu, int n_seqs, int s, int32_t* order) {
+  __shared__ int s_before;
+  if (threadIdx.x == 0) s_before = 0;
+  __syncthreads();
+  const int32_t len = cu[s + 1] - cu[s];
+  int before = 0;
+  for (int j = threadIdx.x; j < n_seqs; j += blockDim.x) {
+    const int32_t lj = cu[j + 1] - cu[j];
+    before += (lj > len || (lj == len && j < s)) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) before += __shfl_xor(before, off);
+  if ((threadIdx.x & 63) == 0 && before != 0) atomicAdd(&s_before, before);
+  __syncthreads();
+  if (threadIdx.x == 0) order[s_before] = s;
+}
+
 // ---------------------------------------------------------------------------
 // Standalone RoPE.  x and y may be the same buffer.
 // ---------------------------------------------------------------------------
@@ -258,11 +281,12 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
                                                           const float* __restrict__ pos, int32_t n_heads,
                                                           RopeTable tab, u32x4* __restrict__ k_ws,
                                                           u32x2* __restrict__ v_ws, float* __restrict__ k_scale,
-                                                          int64_t rows_per_head) {
+                                                          int32_t* __restrict__ order, int64_t rows_per_head) {
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
   __shared__ float s_red[4];
   const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  if (tile == 0 && h == 0) write_segment_rank(cu, int(gridDim.y), s, order);  // before any early exit
   const int32_t seg_a = cu[s];
   const int32_t S = cu[s + 1] - seg_a;
   if (tile * BK >= S) return;  // whole block leaves together
@@ -415,14 +439,16 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const u32x4* __restrict__ k_ws, const u32x4* __restrict__ v_ws, const float* __restrict__ k_scale,
-    int64_t rows_per_head) {
+    const int32_t* __restrict__ order, int64_t rows_per_head) {
   static_assert(P_TILE_CHUNKS == P_NW * 64, "one direct load per wave, tile and tensor");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
 
-  const int qt = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  // The segment comes from the rank order the K/V prologue wrote.
+  const int qt = blockIdx.x, h = blockIdx.y;
+  const int s = gridDim.z == 1 ? 0 : order[blockIdx.z];
   const int32_t seg_a = cu[s];
   const int32_t S = cu[s + 1] - seg_a;
   if (qt * ATTN_BQ >= S) return;  // whole block leaves together
@@ -797,19 +823,20 @@ int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens
 
 int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const float* pos, int64_t /*n_tokens*/,
                        int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws,
-                       void* v_ws, float* k_scale, int64_t rows_per_head, void* stream) {
+                       void* v_ws, float* k_scale, int32_t* order, int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + BK - 1) / BK);
   if (tiles == 0) return 0;
   hipLaunchKernelGGL(kv_prologue_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), cu,
-                     pos, n_heads, table, static_cast<u32x4*>(k_ws), static_cast<u32x2*>(v_ws), k_scale,
+                     pos, n_heads, table, static_cast<u32x4*>(k_ws), static_cast<u32x2*>(v_ws), k_scale, order,
                      rows_per_head);
   return int(hipGetLastError());
 }
 
 int launch_attention(const void* q, const int32_t* cu, const float* pos, void* out, float* lse, int64_t n_tokens,
                      int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
-                     const void* k_ws, const void* v_ws, const float* k_scale, int64_t rows_per_head, void* stream) {
+                     const void* k_ws, const void* v_ws, const float* k_scale, const int32_t* order,
+                     int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + ATTN_BQ - 1) / ATTN_BQ);
   if (tiles == 0) return 0;
   // The dynamic LDS limit is raised once per device.
@@ -825,10 +852,12 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)),
+  // Grid (query tile, head, segment rank): the longest segments go first.
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(tiles, unsigned(n_heads), unsigned(n_seqs)),
                      dim3(P_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
                      pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
-                     static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), k_scale, rows_per_head);
+                     static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), k_scale, order,
+                     rows_per_head);
   return int(hipGetLastError());
 }
 

@@ -148,6 +148,29 @@ __device__ __forceinline__ void stage_rope_table(const RopeTable& tab, float* s_
   }
 }
 
+// Called by every thread of one workgroup per segment s (a block-uniform
+// condition): writes order[rank] = s, where segments rank by length, longest
+// first, equal lengths by index.  That key is a strict total order, so order
+// becomes a permutation of 0 .. n_seqs-1 whatever cu holds.  The attention
+// grid walks it so that the longest segments' workgroups start first and the
+// grid ends on short ones.
+__device__ __forceinline__ void write_segment_rank(const int32_t* cu, int n_seqs, int s, int32_t* order) {
+  __shared__ int s_before;
+  if (threadIdx.x == 0) s_before = 0;
+  __syncthreads();
+  const int32_t len = cu[s + 1] - cu[s];
+  int before = 0;
+  for (int j = threadIdx.x; j < n_seqs; j += blockDim.x) {
+    const int32_t lj = cu[j + 1] - cu[j];
+    before += (lj > len || (lj == len && j < s)) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) before += __shfl_xor(before, off);
+  if ((threadIdx.x & 63) == 0 && before != 0) atomicAdd(&s_before, before);
+  __syncthreads();
+  if (threadIdx.x == 0) order[s_before] = s;
+}
+
 // Row of the packed workspace where segment s's first key lives: every
 // segment starts on a 64-key boundary.
 __device__ __forceinline__ int64_t packed_start(int32_t seg_begin, int32_t s) {

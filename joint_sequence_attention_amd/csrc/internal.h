@@ -37,9 +37,11 @@ inline int64_t packed_rows(int64_t n_tokens, int32_t n_seqs) {
 //   keys    fp16 [H][rows][128]     rotated, each 64-key tile block-scaled
 //   values  bf16 [H][rows/32][128][32]  transposed 32-key tiles
 //   scales  fp32 [H][rows/64]       per-tile factor that undoes the key scaling
+//   order   i32  [n_seqs]           segments by length, longest first (256-byte aligned)
 struct WorkspaceLayout {
-  size_t keys_offset, values_offset, scales_offset, total;
+  size_t keys_offset, values_offset, scales_offset, order_offset, total;
 };
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 inline WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
   const size_t rows = size_t(packed_rows(n_tokens, n_seqs));
   const size_t plane = size_t(n_heads) * rows * kHeadDim * 2;
@@ -47,7 +49,8 @@ inline WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_heads, int32
   w.keys_offset = 0;
   w.values_offset = plane;
   w.scales_offset = 2 * plane;
-  w.total = 2 * plane + size_t(n_heads) * (rows / kKeyTile) * 4;
+  w.order_offset = align256(2 * plane + size_t(n_heads) * (rows / kKeyTile) * 4);
+  w.total = w.order_offset + size_t(n_seqs) * 4;
   return w;
 }
 
@@ -56,8 +59,9 @@ inline WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_heads, int32
 //   values  e4m3 [H][rows/64][128][64]     transposed 64-key tiles
 //   kscale  u32  [H][rows/64]              per tile: 4 exponent scales of 16 keys
 //   vscale  u32  [H][rows/64]              per tile: the exponent scale of its values
+//   order   i32  [n_seqs]                  segments by length, longest first
 struct WorkspaceLayoutFp8 {
-  size_t keys_offset, values_offset, kscale_offset, vscale_offset, total;
+  size_t keys_offset, values_offset, kscale_offset, vscale_offset, order_offset, total;
 };
 inline WorkspaceLayoutFp8 workspace_layout_fp8(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
   const size_t rows = size_t(packed_rows(n_tokens, n_seqs));
@@ -68,7 +72,8 @@ inline WorkspaceLayoutFp8 workspace_layout_fp8(int64_t n_tokens, int32_t n_heads
   w.values_offset = plane;
   w.kscale_offset = 2 * plane;
   w.vscale_offset = 2 * plane + scales;
-  w.total = 2 * plane + 2 * scales;
+  w.order_offset = 2 * plane + 2 * scales;
+  w.total = w.order_offset + size_t(n_seqs) * 4;
   return w;
 }
 
@@ -78,18 +83,18 @@ int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens
                       const RopeTable& table, void* stream);
 int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const float* pos, int64_t n_tokens,
                        int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws,
-                       void* v_ws, float* k_scale, int64_t rows_per_head, void* stream);
+                       void* v_ws, float* k_scale, int32_t* order, int64_t rows_per_head, void* stream);
 int launch_attention(const void* q, const int32_t* cu, const float* pos, void* out, float* lse, int64_t n_tokens,
                      int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale, const RopeTable& table,
-                     const void* k_ws, const void* v_ws, const float* k_scale, int64_t rows_per_head,
-                     void* stream);
+                     const void* k_ws, const void* v_ws, const float* k_scale, const int32_t* order,
+                     int64_t rows_per_head, void* stream);
 int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, const float* pos, int32_t n_heads,
                            int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws, void* v_ws,
-                           unsigned* k_sc, unsigned* v_sc, int64_t rows_per_head, void* stream);
+                           unsigned* k_sc, unsigned* v_sc, int32_t* order, int64_t rows_per_head, void* stream);
 int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
                          int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
                          float skip_threshold, const RopeTable& table, const void* k_ws, const void* v_ws,
-                         const unsigned* k_sc, const unsigned* v_sc, int64_t rows_per_head,
+                         const unsigned* k_sc, const unsigned* v_sc, const int32_t* order, int64_t rows_per_head,
                          unsigned long long* skip_stats, void* stream);
 const char* hip_error_string(int err);
 
