@@ -45,17 +45,17 @@ SKIP_AMPLITUDE = 20.0      # q/k amplitude of the local-attention inputs the ski
 HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
-    "source_sha256": "9366769e62c1312667b7c8ff4f6fb85a7c744449a015821655e59cff14e2d5a9",
-    "fetch_kib": 4438712, "fetch_scale": 2.0,
-    "write_kib": 165110, "write_scale": 1.0,
+    "source_sha256": "b48f78820431361872a025534ce2334cf90c44c6b34fc066d6c1d204f3814f63",
+    "fetch_kib": 5501807, "fetch_scale": 2.0,
+    "write_kib": 165124, "write_scale": 1.0,
 }
 # The same for attn_fwd_fp8_kernel (dense instance, N(0, 1) inputs).
 FP8_HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_fp8.hip"),
-    "source_sha256": "7f6f33bbf3a8be70e7ff3e6482dd7cad206ce71c412d9dd835ae5b0d21b6ce7a",
-    "fetch_kib": 2057167, "fetch_scale": 2.0,
-    "write_kib": 297350, "write_scale": 1.0,
+    "source_sha256": "d6c80f0934d5287e6e0945e88294ae0a4c5ae40d3e845d675ecb0bad6dd26298",
+    "fetch_kib": 2109386, "fetch_scale": 2.0,
+    "write_kib": 297305, "write_scale": 1.0,
 }
 
 
