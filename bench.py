@@ -120,7 +120,7 @@ def cpu_baseline(c, flop_per_row_head, target_seconds=15.0):
                       f"({t_used:.1f} s of float64 oracle time; FLOP counted as 4*S*d per row and head)"}
 
 
-def survey_workload(name, steps, warmup):
+def workload_line(name, steps, warmup):
     """Time one workload: the whole path, the attention kernel alone and the standalone RoPE kernel."""
     import numpy as np
     import torch
@@ -233,7 +233,7 @@ def main():
         sys.exit(2)
     if args.all_workloads:
         for name in wl.CONFIG_ORDER:
-            print(json.dumps(survey_workload(name, args.steps, args.warmup)), flush=True)
+            print(json.dumps(workload_line(name, args.steps, args.warmup)), flush=True)
         return
     dev = torch.device("cuda:0")
     name = args.workload
