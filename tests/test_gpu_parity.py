@@ -85,6 +85,21 @@ def test_rope_apply_in_place_matches_out_of_place(gpu):
     assert np.array_equal(bf16_bits(x), bf16_bits(y))
 
 
+def test_rope_apply_at_the_origin_returns_its_input(gpu):
+    # Every angle at position (0, 0, 0) is +0, whose sine and cosine are exactly 0 and 1, so the
+    # rotation there is the identity: the output equals the input value for value. The refiner's
+    # text rows all sit at the origin; the tiny workload's first video token does too, inside a
+    # wave of other tokens.
+    for name in ("refiner", "tiny"):
+        cfg = wl.config(name)
+        c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
+        at0 = np.all(c.pos == 0, axis=1)
+        say(f"rope_apply at the origin, {name}: {int(at0.sum())} of {c.N} tokens")
+        assert at0.any()
+        y = widen(bf16_bits(H.h3attn_rope_apply(c.q, c.pos_d)))
+        assert np.array_equal(y[at0], widen(c.qb)[at0])
+
+
 @pytest.mark.parametrize("seed", [1, 1001])
 def test_tiny_full(gpu, seed):
     cfg = wl.config("tiny")
