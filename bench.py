@@ -45,7 +45,7 @@ SKIP_AMPLITUDE = 20.0      # q/k amplitude of the local-attention inputs the ski
 HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
-    "source_sha256": "b48f78820431361872a025534ce2334cf90c44c6b34fc066d6c1d204f3814f63",
+    "source_sha256": "0ba46a8560de2539116e7146d199a5317e99f07daa800e5993b99f56c2b2d44e",
     "fetch_kib": 5501807, "fetch_scale": 2.0,
     "write_kib": 165124, "write_scale": 1.0,
 }
@@ -53,7 +53,7 @@ HBM_COUNTERS = {
 FP8_HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_fp8.hip"),
-    "source_sha256": "d6c80f0934d5287e6e0945e88294ae0a4c5ae40d3e845d675ecb0bad6dd26298",
+    "source_sha256": "479dcf69aeb9c3f822b9ce71ebff4d6e14c0b46165b431a1ebe95f647a873b9f",
     "fetch_kib": 2109386, "fetch_scale": 2.0,
     "write_kib": 297305, "write_scale": 1.0,
 }

@@ -13,8 +13,9 @@
 //   kv_prologue_fp8_kernel  rotates K, quantizes it in 16-key blocks and V in
 //                           64-key blocks (power-of-two scales), and packs
 //                           both into 64-key tiles, V transposed.  HBM-bound.
-//   attn_fwd_fp8_kernel     one workgroup per (256-query tile, segment, head),
-//                           eight waves, 32 queries per wave; 64-key tiles
+//   attn_fwd_fp8_kernel     one workgroup per (256-query tile, head, segment
+//                           rank), longest segments first; eight waves, 32
+//                           queries per wave; 64-key tiles
 //                           through LDS rings; both contractions on
 //                           v_mfma_scale_f32_32x32x64_f8f6f4.
 //

@@ -13,8 +13,9 @@
 //   kv_prologue_kernel  rotates K once per call and packs it, with V
 //                       transposed, into 64-key tiles that start on a 64-key
 //                       boundary for every segment.  HBM-bound.
-//   attn_fwd_kernel     one workgroup per (256-query tile, segment, head).
-//                       It rotates its queries while loading them, then
+//   attn_fwd_kernel     one workgroup per (256-query tile, head, segment
+//                       rank), longest segments first (the prologue ranks
+//                       them).  It rotates its queries while loading them, then
 //                       streams the segment's 32-key tiles through LDS and
 //                       runs an online softmax between two MFMA contractions,
 //                       software-pipelined inside each wave.
