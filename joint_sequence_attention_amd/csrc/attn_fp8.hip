@@ -362,7 +362,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) voff[hf] = F8_VBASE + v8_lds_offset(l32, 2 * g + hf);
   // The 16-key block of the keys this lane feeds, per subtile: 2u + (l32 >= 16).
-  const unsigned ksh0 = l32 >= 16 ? 8u : 0u, ksh1 = ksh0 + 16u;
+  const unsigned ksh0 = l32 >= 16 ? 8u : 0u;
 
   f32x16 o[4];
 #pragma unroll
@@ -398,17 +398,20 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     const u32x4 b = *reinterpret_cast<const u32x4*>(base + voff[1]);
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto mfma_qk = [&](f32x16 acc, i32x8 kf, int ks, unsigned ksc) __attribute__((always_inline)) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 0, int(ksc), 0, int(qsc));
+  // ksw holds the lane's key scales of subtiles 0 and 1 in bytes 0 and 2; the
+  // instruction's scale byte select picks one, so no per-subtile extraction.
+  auto mfma_qk = [&](f32x16 acc, i32x8 kf, int ks, int u, unsigned ksw) __attribute__((always_inline)) {
+    if (u == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 0, int(ksw), 0, int(qsc));
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 2, int(ksw), 0, int(qsc));
   };
   auto mfma_pv = [&](f32x16 acc, i32x8 vf, const i32x8& p, unsigned vsc) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, p, acc, 0, 0, 0, int(vsc), 0, E8M0_ONE);
   };
-  // Per-lane exponent scales of K tile t for subtiles 0 and 1, and V tile t's.
+  // Per-lane exponent scales of K tile t (subtile 0 in byte 0, subtile 1 in
+  // byte 2, both in k0; k1 carries the same word), and V tile t's.
   auto kscales = [&](int t, unsigned& k0, unsigned& k1) __attribute__((always_inline)) {
-    const unsigned w = ksp[t];
-    k0 = (w >> ksh0) & 0xffu;
-    k1 = (w >> ksh1) & 0xffu;
+    k0 = ksp[t] >> ksh0;
+    k1 = k0;
   };
   auto vscale = [&](int t) __attribute__((always_inline)) { return vsp[t]; };
 
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = START_AT_M ? -moff : 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acc = mfma_qk(acc, kfrag(SLOT, u, ks), ks, u ? k1 : k0);
+      for (int ks = 0; ks < 2; ++ks) acc = mfma_qk(acc, kfrag(SLOT, u, ks), ks, u, u ? k1 : k0);
       sc[b][u] = acc;
     }
   };
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           } else {
             acc = sc[1 - b][u];
           }
-          sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u ? k1 : k0);
+          sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u, u ? k1 : k0);
           if (j < 2)
             fr[u] = kfrag(kslot, u, 1);
           else if (do_pv)
@@ -603,7 +606,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           } else {
             acc = sc[1 - b][u];
           }
-          sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u ? k1 : k0);
+          sc[1 - b][u] = mfma_qk(acc, fr[u], ks, u, u ? k1 : k0);
           // next fragment into the register this MFMA has read
           if (j < 2)
             fr[u] = kfrag(kslot, u, 1);
