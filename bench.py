@@ -46,16 +46,16 @@ HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
     "source_sha256": "0ba46a8560de2539116e7146d199a5317e99f07daa800e5993b99f56c2b2d44e",
-    "fetch_kib": 5501807, "fetch_scale": 2.0,
-    "write_kib": 165124, "write_scale": 1.0,
+    "fetch_kib": 5095285, "fetch_scale": 2.0,
+    "write_kib": 165121, "write_scale": 1.0,
 }
 # The same for attn_fwd_fp8_kernel (dense instance, N(0, 1) inputs).
 FP8_HBM_COUNTERS = {
     "workload": "1344x768",
     "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_fp8.hip"),
-    "source_sha256": "479dcf69aeb9c3f822b9ce71ebff4d6e14c0b46165b431a1ebe95f647a873b9f",
-    "fetch_kib": 2109386, "fetch_scale": 2.0,
-    "write_kib": 297305, "write_scale": 1.0,
+    "source_sha256": "ac92d5ec4c7afd7494eab5d5020645283bfb2d3bceb7ec60d58848cbf23dae79",
+    "fetch_kib": 2022873, "fetch_scale": 2.0,
+    "write_kib": 210878, "write_scale": 1.0,
 }
 
 
