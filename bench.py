@@ -11,7 +11,10 @@ value = algorithmic FLOP per step (4 * S^2 * d per segment and head) / mean step
 time.  roofline: the attention kernel alone, timed with HIP events recorded on
 the stream it is launched on, against the bf16 dense MFMA peak.
 cpu_baseline: the float64 oracle on a bounded sample of query rows of the same
-workload, on this host's cores.
+workload, on this host's cores ("cores" = the BLAS threads it ran on, beside the
+host's CPU count and the size of this process's CPU affinity set).
+roofline counters (mfma_busy, clock_ghz, traffic, hbm_gbps): a rocprofv3 --pmc
+pass over child runs of this script, unless --no-counters.
 fp8_mode: the same step through the lossy FP8 entry points (h3attn_varlen_fwd_fp8:
 e4m3 Q/K/P/V with block scales), with its own roofline against the fp8 dense
 MFMA peak.  It is reported beside the bf16 metric, never in its place.
@@ -38,41 +41,115 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 SKIP_THRESHOLD = 0.05      # the recipe's Skip-Softmax threshold
 SKIP_AMPLITUDE = 20.0      # q/k amplitude of the local-attention inputs the skip mode is timed on
 
-# HBM bytes of one attn_fwd_kernel launch on the 1344x768 workload, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
-# plain 1 GiB device copy (FETCH_SIZE reports half of the bytes read, WRITE_SIZE all bytes written).
-# The figures hold only for the kernel source they were taken on; any other source reports null.
-HBM_COUNTERS = {
-    "workload": "1344x768",
-    "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_kernels.hip"),
-    "source_sha256": "0ba46a8560de2539116e7146d199a5317e99f07daa800e5993b99f56c2b2d44e",
-    "fetch_kib": 5095285, "fetch_scale": 2.0,
-    "write_kib": 165121, "write_scale": 1.0,
-}
-# The same for attn_fwd_fp8_kernel (dense instance, N(0, 1) inputs).
-FP8_HBM_COUNTERS = {
-    "workload": "1344x768",
-    "source": os.path.join("joint_sequence_attention_amd", "csrc", "attn_fp8.hip"),
-    "source_sha256": "ac92d5ec4c7afd7494eab5d5020645283bfb2d3bceb7ec60d58848cbf23dae79",
-    "fetch_kib": 2022873, "fetch_scale": 2.0,
-    "write_kib": 210878, "write_scale": 1.0,
-}
+# Hardware-counter pass (on by default, --no-counters to skip): bench.py runs itself again as
+# `rocprofv3 --pmc <counters> -- python3 bench.py --counter-pass`, one child process per counter
+# group, and reads the per-dispatch means of the attention kernels from rocprofv3's CSV.
+#   * SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (with the kernel trace of the same run): share of
+#     SIMD cycles the matrix cores are busy, and the mean graphics clock of the launches;
+#   * FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, one counter group per run): HBM-side bytes.
+#     Each is scaled by what it reads for a plain device copy of known size: FETCH_SIZE reports
+#     half of the bytes read (factor 2), WRITE_SIZE all bytes written (factor 1), measured with
+#     `bench.py --copy-calibration-mib 1024` under the same counters.
+COUNTER_GROUPS = (("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"), ("FETCH_SIZE",), ("WRITE_SIZE",))
+FETCH_SCALE = 2.0
+WRITE_SCALE = 1.0
+N_XCD = 8                  # GRBM_GUI_ACTIVE is summed over the XCDs
+SIMDS_PER_CU = 4
+KERNELS = {"bf16": "attn_fwd_kernel(", "fp8": "attn_fwd_fp8_kernel<false>"}
 
 
-def counted_traffic(workload, c=HBM_COUNTERS):
-    """Calibrated HBM bytes per attention launch, or None when the counters do not apply."""
-    import hashlib
+def _find_csv(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    return hits[0] if hits else None
 
-    if workload != c["workload"]:
-        return None
-    try:
-        with open(os.path.join(ROOT, c["source"]), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
-        return None
-    if digest != c["source_sha256"]:
-        return None
-    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+
+def parse_counter_csv(path):
+    """rocprofv3 counter_collection.csv -> {kernel key: {counter: mean value per dispatch}}."""
+    import csv
+    sums, counts = {}, {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            for key, pat in KERNELS.items():
+                if pat in name:
+                    c = row["Counter_Name"]
+                    sums.setdefault(key, {}).setdefault(c, 0.0)
+                    counts.setdefault(key, {}).setdefault(c, 0)
+                    sums[key][c] += float(row["Counter_Value"])
+                    counts[key][c] += 1
+    return {k: {c: sums[k][c] / counts[k][c] for c in sums[k]} for k in sums}
+
+
+def parse_kernel_trace_csv(path):
+    """rocprofv3 kernel_trace.csv -> {kernel key: mean duration in seconds}."""
+    import csv
+    durs = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            for key, pat in KERNELS.items():
+                if pat in name:
+                    durs.setdefault(key, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9)
+    return {k: sum(v) / len(v) for k, v in durs.items()}
+
+
+def run_counter_passes(name, timeout_s=240.0):
+    """One rocprofv3 --pmc child run per counter group; returns {kernel key: {counter: value}} and notes."""
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+
+    rocprof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    merged, durations, notes = {}, {}, []
+    base = tempfile.mkdtemp(prefix="h3attn_counters_")
+    for i, group in enumerate(COUNTER_GROUPS):
+        d = os.path.join(base, f"pass{i}")
+        cmd = [rocprof, "--pmc", *group]
+        if i == 0:
+            cmd.append("--kernel-trace")
+        cmd += ["--output-format", "csv", "-d", d, "-o", "run", "--",
+                sys.executable, os.path.abspath(__file__), "--counter-pass", "--workload", name]
+        print(f"[bench] counter pass {i + 1}/{len(COUNTER_GROUPS)}: {' '.join(group)}", file=sys.stderr, flush=True)
+        proc = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True,
+                                start_new_session=True, cwd=base)
+        try:
+            _, err = proc.communicate(timeout=timeout_s)
+        except subprocess.TimeoutExpired:
+            os.killpg(proc.pid, signal.SIGKILL)
+            proc.communicate()
+            notes.append(f"{' '.join(group)}: no result within {timeout_s:.0f} s")
+            continue
+        path = _find_csv(d, "counter_collection.csv")
+        if path is None:
+            notes.append(f"{' '.join(group)}: rocprofv3 exit {proc.returncode}, no counter file "
+                         f"({(err or '').strip().splitlines()[-1:]})")
+            continue
+        for k, vals in parse_counter_csv(path).items():
+            merged.setdefault(k, {}).update(vals)
+        if i == 0:
+            trace = _find_csv(d, "kernel_trace.csv")
+            if trace:
+                durations = parse_kernel_trace_csv(trace)
+    shutil.rmtree(base, ignore_errors=True)
+    return merged, durations, notes
+
+
+def counter_fields(counters, durations, key, kernel_ms, n_cu):
+    """mfma_busy, clock_ghz, traffic and hbm_gbps for one attention kernel (None where not measured)."""
+    c = counters.get(key, {})
+    out = {"mfma_busy": None, "clock_ghz": None, "traffic": None, "hbm_gbps": None}
+    busy, grbm = c.get("SQ_VALU_MFMA_BUSY_CYCLES"), c.get("GRBM_GUI_ACTIVE")
+    if busy is not None and grbm:
+        out["mfma_busy"] = round(busy / (grbm / N_XCD * n_cu * SIMDS_PER_CU), 4)
+        if durations.get(key):
+            out["clock_ghz"] = round(grbm / N_XCD / durations[key] / 1e9, 3)
+    fetch, write = c.get("FETCH_SIZE"), c.get("WRITE_SIZE")
+    if fetch is not None and write is not None:
+        out["traffic"] = int(round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024))
+        out["hbm_gbps"] = round(out["traffic"] / (kernel_ms * 1e-3) / 1e9, 1)
+    return out
 
 
 METRIC = "joint A/V attention TFLOP/s @ ~130k tokens; % of bf16 MFMA peak"
@@ -115,7 +192,12 @@ def cpu_baseline(c, flop_per_row_head, target_seconds=15.0):
         rows_done += batch
         batch = min(batch * 2, 256)
     flop = rows_done * c["heads"] * flop_per_row_head
-    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"value": flop / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": affinity, "kind": "oracle",
             "sample": f"{rows_done} random query rows x {c['heads']} heads, each against all keys of its segment "
                       f"({t_used:.1f} s of float64 oracle time; FLOP counted as 4*S*d per row and head)"}
 
@@ -199,6 +281,10 @@ def main():
     ap.add_argument("--workload", default="1344x768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 counter pass (mfma_busy, clock_ghz, traffic, hbm_gbps become null)")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="internal: the child run profiled by the counter pass (a few steps of each kernel)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
     ap.add_argument("--all-workloads", action="store_true",
@@ -234,6 +320,9 @@ def main():
     if args.all_workloads:
         for name in wl.CONFIG_ORDER:
             print(json.dumps(workload_line(name, args.steps, args.warmup)), flush=True)
+        return
+    if args.counter_pass:
+        counter_pass_child(args.workload)
         return
     dev = torch.device("cuda:0")
     name = args.workload
@@ -323,7 +412,6 @@ def main():
            "ms_per_step": round(fp8_ms_per_step, 4), "dtype": "fp8 e4m3 operands, fp32 accumulate",
            "roofline": {"bound": "mfma", "achieved": round(fp8_achieved, 2), "peak": PEAK_FP8_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(fp8_achieved / PEAK_FP8_TFLOPS, 4),
-                        "traffic": counted_traffic(name, FP8_HBM_COUNTERS),
                         "kernel": "attn_fwd_fp8_kernel", "kernel_ms": round(fp8_attn_ms, 4)}}
 
     # Skip-Softmax (FP8 mode, threshold 0.05 as in the recipe) on inputs whose attention is local:
@@ -386,12 +474,55 @@ def main():
         "config": describe(name, cfg, N, len(lens)),
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counted_traffic(name),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
         "fp8_mode": fp8,
     }
+    # Hardware counters of both attention kernels from rocprofv3 child runs of this script.
+    counters, durations, notes = ({}, {}, ["--no-counters"]) if args.no_counters else run_counter_passes(name)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rec["roofline"].update(counter_fields(counters, durations, "bf16", attn_ms, n_cu))
+    fp8["roofline"].update(counter_fields(counters, durations, "fp8", fp8_attn_ms, n_cu))
+    rec["roofline"]["counters"] = {
+        "source": "rocprofv3 --pmc, child runs of bench.py --counter-pass (3 steps per kernel)",
+        "mfma_busy": "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 4 SIMDs x CUs)",
+        "clock_ghz": "GRBM_GUI_ACTIVE / 8 XCDs / traced kernel duration",
+        "traffic": f"(FETCH_SIZE x {FETCH_SCALE} + WRITE_SIZE x {WRITE_SCALE}) KiB per dispatch, copy-calibrated",
+        "hbm_gbps": "traffic / kernel_ms", "notes": notes}
+    for key, r in (("bf16", rec["roofline"]), ("fp8", fp8["roofline"])):
+        print(f"[bench] counters {key}: mfma_busy {r['mfma_busy']}, clock {r['clock_ghz']} GHz, "
+              f"traffic {r['traffic']} B, {r['hbm_gbps']} GB/s", file=sys.stderr, flush=True)
     print(json.dumps(rec), flush=True)
+
+
+def counter_pass_child(name, steps=3):
+    """A short run of both attention paths on the workload, for rocprofv3 to count."""
+    import numpy as np
+    import torch
+
+    from joint_sequence_attention_amd import h3attn as H
+    from joint_sequence_attention_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    cfg = wl.config(name)
+    cu, pos = H.h3attn_build_layout(cfg["segments"])
+    N, heads = int(cu[-1]), cfg["heads"]
+    lens = np.diff(cu.astype(np.int64))
+    max_seqlen = int(lens.max())
+    q, k, v = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+               for b in wl.random_qkv(N, heads, cfg["seed"]))
+    cu_d = torch.from_numpy(cu).to(dev)
+    pos_d = torch.from_numpy(np.ascontiguousarray(pos)).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((heads, N), dtype=torch.float32, device=dev)
+    ws = H.alloc_workspace(N, heads, len(lens), dev)
+    ws8 = H.alloc_workspace(N, heads, len(lens), dev, fp8=True)
+    for _ in range(steps + 1):
+        H.h3attn_varlen_fwd(q, k, v, cu_d, pos_d, max_seqlen, out=out, lse=lse, workspace=ws)
+    for _ in range(steps + 1):
+        H.h3attn_varlen_fwd_fp8(q, k, v, cu_d, pos_d, max_seqlen, out=out, lse=lse, workspace=ws8)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -131,10 +131,12 @@ h3attn_status h3attn_rope_apply(const void* x, void* y, const float* pos_thw, in
  *   lse[h, i] = ln sum_j exp(scale * <rope(q)[i,h], rope(k)[j,h]>)
  *
  * with i, j ranging over the same segment [cu[s], cu[s+1]) and no causal
- * order.  scale <= 0 selects 1/sqrt(D).  max_seqlen must be >= every
- * segment's length (rows of a longer segment are not computed).  Empty
- * segments produce no rows; N = 0 is a no-op.  out and lse must not
- * overlap any input.
+ * order.  scale <= 0 selects 1/sqrt(D).  max_seqlen is the longest segment
+ * length the call computes, at most 2^22 = 4,194,304 (UNSUPPORTED above) and
+ * at most N: a segment longer than max_seqlen is computed as its first
+ * max_seqlen tokens alone, so its later rows of out and lse are not written
+ * and its later keys are not attended.  Empty segments produce no rows; N = 0
+ * is a no-op.  out and lse must not overlap any input.
  *
  * The workspace (device, >= h3attn_varlen_fwd_workspace_size bytes, 256-byte
  * aligned) holds the rotated keys (fp16, each 64-key tile scaled by a power

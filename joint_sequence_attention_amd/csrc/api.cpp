@@ -63,6 +63,7 @@ h3attn_status check_varlen(int64_t n_tokens, int32_t n_heads, int32_t head_dim, 
   if (n_seqs > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "n_seqs above 65535");
   if (max_seqlen < 0) return fail(H3ATTN_ERR_INVALID_ARG, "max_seqlen must be >= 0");
   if (max_seqlen > n_tokens) return fail(H3ATTN_ERR_INVALID_ARG, "max_seqlen exceeds n_tokens");
+  if (max_seqlen > kMaxSeqlen) return fail(H3ATTN_ERR_UNSUPPORTED, "max_seqlen above 4,194,304 (2^22) tokens");
   return H3ATTN_OK;
 }
 

@@ -91,14 +91,15 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
                                                               RopeTable tab, u32x2* __restrict__ k_ws,
                                                               unsigned* __restrict__ v_ws,
                                                               unsigned* __restrict__ k_sc, unsigned* __restrict__ v_sc,
-                                                              int32_t* __restrict__ order, int64_t rows_per_head) {
+                                                              int32_t* __restrict__ order, int64_t rows_per_head,
+                                                              int32_t max_seqlen) {
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
   __shared__ float s_red[4][5];
   const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   if (tile == 0 && h == 0) write_segment_rank(cu, int(gridDim.y), s, order);  // before any early exit
   const int32_t seg_a = cu[s];
-  const int32_t S = cu[s + 1] - seg_a;
+  const int32_t S = min(cu[s + 1] - seg_a, max_seqlen);  // a longer segment counts as its first max_seqlen tokens
   if (tile * KT >= S) return;  // whole block leaves together
   stage_rope_table(tab, s_omega, s_axis);
   __syncthreads();
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const char* __restrict__ k_ws, const char* __restrict__ v_ws,
     const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_sc, const int32_t* __restrict__ order,
-    int64_t rows_per_head, float skip_log2, unsigned long long* __restrict__ skip_stats) {
+    int64_t rows_per_head, int32_t max_seqlen, float skip_log2, unsigned long long* __restrict__ skip_stats) {
   static_assert(F8_TILE_BYTES / 16 == F8_NW * 64, "one direct load per lane, tile and tensor");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   const int qt = blockIdx.x, h = blockIdx.y;
   const int s = gridDim.z == 1 ? 0 : order[blockIdx.z];
   const int32_t seg_a = cu[s];
-  const int32_t S = cu[s + 1] - seg_a;
+  const int32_t S = min(cu[s + 1] - seg_a, max_seqlen);  // a longer segment counts as its first max_seqlen tokens
   if (qt * F8_BQ >= S) return;  // whole block leaves together
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -792,7 +793,7 @@ int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, cons
   hipLaunchKernelGGL(kv_prologue_fp8_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                      cu, pos, n_heads, table, static_cast<u32x2*>(k_ws), static_cast<unsigned*>(v_ws), k_sc, v_sc,
-                     order, rows_per_head);
+                     order, rows_per_head, max_seqlen);
   return int(hipGetLastError());
 }
 
@@ -825,13 +826,13 @@ int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, voi
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, grid, dim3(F8_NW * 64), F8_SMEM, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(q), cu, pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens),
                        n_heads, scale_log2, table, static_cast<const char*>(k_ws), static_cast<const char*>(v_ws),
-                       k_sc, v_sc, order, rows_per_head, skip_log2, skip_stats);
+                       k_sc, v_sc, order, rows_per_head, max_seqlen, skip_log2, skip_stats);
   else
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, grid, dim3(F8_NW * 64), F8_SMEM,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu, pos,
                        static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
                        static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_sc, order,
-                       rows_per_head, 0.0f, nullptr);
+                       rows_per_head, max_seqlen, 0.0f, nullptr);
   return int(hipGetLastError());
 }
 

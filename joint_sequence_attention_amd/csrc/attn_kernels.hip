@@ -42,42 +42,21 @@
 // already turns raw scores into base-2 logits, so the inner loop pays nothing
 // for them.  P and V stay bf16 for the second contraction.
 
-#include <hip/hip_runtime.h>
-
 #include <atomic>
 #include <cmath>
-#include <cstdint>
-#include <type_traits>
 
-#include "internal.h"
+#include "device_common.h"
 
 namespace h3attn {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+using namespace dev;
+
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 
-constexpr int D = kHeadDim;
-constexpr int BK = kKeyTile;                    // keys per tile
-constexpr int CHUNKS_PER_ROW = D / 8;           // 16-byte chunks per 128-dim row
-constexpr int TILE_CHUNKS = BK * CHUNKS_PER_ROW;  // 1024 chunks = 16 KiB per tile
-constexpr int VT = 32;                           // keys per transposed value tile
-
-__device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
-
-// Two floats -> two bf16 (round to nearest even), low half first.
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  bf16x2 v;
-  v[0] = static_cast<__bf16>(a);
-  v[1] = static_cast<__bf16>(b);
-  return __builtin_bit_cast(unsigned, v);
-}
+constexpr int BK = kKeyTile;  // keys per packed workspace tile
+constexpr int VT = 32;        // keys per transposed value tile
 
 // Two floats -> two fp16 (round to nearest even), low half first.
 __device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
@@ -118,101 +97,11 @@ __device__ __forceinline__ float amax8(const float (&f)[8], float m) {
   return m;
 }
 
-__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf_lo(v[i]);
-    f[2 * i + 1] = bf_hi(v[i]);
-  }
-}
-
 __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   u32x4 v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
   return v;
-}
-
-// Rotation of 4 consecutive pairs (dims 2*pair0 .. 2*pair0+7) in fp32.  Pair
-// p turns by phi = pos[axis(p)] * omega(p); (x0, x1) -> (x0 cos - x1 sin,
-// x0 sin + x1 cos).  The angles depend on the token only, not on the head.
-// Every caller goes through these two functions, so the standalone RoPE and
-// the rotations fused into the attention path round identically.
-struct Rot4 {
-  float sn[4], cs[4];
-};
-
-__device__ __forceinline__ Rot4 rope_angles4(int pair0, const float* s_omega, const int* s_axis, float pt, float ph,
-                                             float pw) {
-  Rot4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = pair0 + i;
-    const int ax = s_axis[p];
-    const float ps = ax == 0 ? pt : (ax == 1 ? ph : pw);
-    const float phi = ps * s_omega[p];
-    sincosf(phi, &r.sn[i], &r.cs[i]);
-  }
-  return r;
-}
-
-__device__ __forceinline__ void rope_turn4(float (&x)[8], const Rot4& r) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float x0 = x[2 * i], x1 = x[2 * i + 1];
-    x[2 * i] = fmaf(x0, r.cs[i], -(x1 * r.sn[i]));
-    x[2 * i + 1] = fmaf(x0, r.sn[i], x1 * r.cs[i]);
-  }
-}
-
-// A token at position (0, 0, 0) turns every pair by angle 0, the identity
-// (sin 0 = 0 and cos 0 = 1 are exact), so its rows may be left as they are.
-// The test is taken per wave: when every active lane holds such a token (a
-// wave of text rows) the angles are skipped with one scalar branch; a wave
-// with any other token turns all its lanes, which changes no value of a
-// lane at the origin except the sign of a zero.
-__device__ __forceinline__ bool at_origin(float pt, float ph, float pw) {
-  return pt == 0.0f && ph == 0.0f && pw == 0.0f;
-}
-
-__device__ __forceinline__ bool wave_at_origin(float pt, float ph, float pw) {
-  return __builtin_amdgcn_ballot_w64(!at_origin(pt, ph, pw)) == 0;
-}
-
-__device__ __forceinline__ void rope8(float (&x)[8], int pair0, const float* s_omega, const int* s_axis,
-                                      float pt, float ph, float pw) {
-  if (wave_at_origin(pt, ph, pw)) return;
-  rope_turn4(x, rope_angles4(pair0, s_omega, s_axis, pt, ph, pw));
-}
-
-__device__ __forceinline__ void stage_rope_table(const RopeTable& tab, float* s_omega, int* s_axis) {
-  if (threadIdx.x < kPairs) {
-    s_omega[threadIdx.x] = tab.omega[threadIdx.x];
-    s_axis[threadIdx.x] = tab.axis[threadIdx.x];
-  }
-}
-
-// Called by every thread of one workgroup per segment s (a block-uniform
-// condition): writes order[rank] = s, where segments rank by length, longest
-// first, equal lengths by index.  That key is a strict total order, so order
-// becomes a permutation of 0 .. n_seqs-1 whatever cu holds.  The attention
-// grid walks it so that the longest segments' workgroups start first and the
-// grid ends on short ones.
-__device__ __forceinline__ void write_segment_rank(const int32_t* cu, int n_seqs, int s, int32_t* order) {
-  __shared__ int s_before;
-  if (threadIdx.x == 0) s_before = 0;
-  __syncthreads();
-  const int32_t len = cu[s + 1] - cu[s];
-  int before = 0;
-  for (int j = threadIdx.x; j < n_seqs; j += blockDim.x) {
-    const int32_t lj = cu[j + 1] - cu[j];
-    before += (lj > len || (lj == len && j < s)) ? 1 : 0;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) before += __shfl_xor(before, off);
-  if ((threadIdx.x & 63) == 0 && before != 0) atomicAdd(&s_before, before);
-  __syncthreads();
-  if (threadIdx.x == 0) order[s_before] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -264,11 +153,6 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const u32x4* x, u32x4* 
   }
 }
 
-// Row of the packed workspace where segment s's first key lives.
-__device__ __forceinline__ int64_t packed_start(int32_t seg_begin, int32_t s) {
-  return int64_t(BK) * ((int64_t(seg_begin) + BK - 1) / BK + s);
-}
-
 // ---------------------------------------------------------------------------
 // K/V prologue.  grid = (key tiles of the longest segment, segments, heads).
 // k_ws: [H][rows][128] rotated keys as fp16, each 64-key tile scaled by a
@@ -282,14 +166,15 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
                                                           const float* __restrict__ pos, int32_t n_heads,
                                                           RopeTable tab, u32x4* __restrict__ k_ws,
                                                           u32x2* __restrict__ v_ws, float* __restrict__ k_scale,
-                                                          int32_t* __restrict__ order, int64_t rows_per_head) {
+                                                          int32_t* __restrict__ order, int64_t rows_per_head,
+                                                          int32_t max_seqlen) {
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
   __shared__ float s_red[4];
   const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   if (tile == 0 && h == 0) write_segment_rank(cu, int(gridDim.y), s, order);  // before any early exit
   const int32_t seg_a = cu[s];
-  const int32_t S = cu[s + 1] - seg_a;
+  const int32_t S = min(cu[s + 1] - seg_a, max_seqlen);  // a longer segment counts as its first max_seqlen tokens
   if (tile * BK >= S) return;  // whole block leaves together
   stage_rope_table(tab, s_omega, s_axis);
   __syncthreads();
@@ -362,18 +247,6 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const u32x4* __restric
   }
 }
 
-// Max / sum with the partner lane (L ^ 32) that holds the other 16 keys.
-__device__ __forceinline__ float pair_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // ---------------------------------------------------------------------------
 // Attention forward, software-pipelined inside each wave.
 //
@@ -407,8 +280,6 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ int k_lds_offset(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_lds_offset(int d, int c) { return d * 64 + 16 * (c ^ ((d >> 2) & 3)); }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr int PK = 32;                              // keys per tile
 constexpr int P_NW = 8;                             // waves per workgroup
 constexpr int ATTN_BQ = 32 * P_NW;                  // 256 query rows per workgroup
@@ -419,28 +290,11 @@ constexpr int P_VBASE = P_NS * P_TILE_BYTES;        // value ring after the key 
 constexpr size_t ATTN_SMEM = 2 * P_NS * P_TILE_BYTES;  // 128 KiB
 constexpr float LAZY_LOG2 = 16.0f;                  // log2 of the largest row sum left unrescaled
 
-template <int N>
-using ic = std::integral_constant<int, N>;
-
-// Wait until at most N vector-memory operations of this wave are in flight,
-// then meet the other waves.  The memory clobber keeps the compiler from
-// moving LDS accesses across it.
-template <int N>
-__device__ __forceinline__ void ring_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Pins a value to the point where this is called: the compiler may neither
-// compute it later nor fold it into later code.
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
-
 __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const u32x4* __restrict__ k_ws, const u32x4* __restrict__ v_ws, const float* __restrict__ k_scale,
-    const int32_t* __restrict__ order, int64_t rows_per_head) {
+    const int32_t* __restrict__ order, int64_t rows_per_head, int32_t max_seqlen) {
   static_assert(P_TILE_CHUNKS == P_NW * 64, "one direct load per wave, tile and tensor");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -451,7 +305,7 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
   const int qt = blockIdx.x, h = blockIdx.y;
   const int s = gridDim.z == 1 ? 0 : order[blockIdx.z];
   const int32_t seg_a = cu[s];
-  const int32_t S = cu[s + 1] - seg_a;
+  const int32_t S = min(cu[s + 1] - seg_a, max_seqlen);  // a longer segment counts as its first max_seqlen tokens
   if (qt * ATTN_BQ >= S) return;  // whole block leaves together
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -830,7 +684,7 @@ int launch_kv_prologue(const void* k, const void* v, const int32_t* cu, const fl
   hipLaunchKernelGGL(kv_prologue_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), cu,
                      pos, n_heads, table, static_cast<u32x4*>(k_ws), static_cast<u32x2*>(v_ws), k_scale, order,
-                     rows_per_head);
+                     rows_per_head, max_seqlen);
   return int(hipGetLastError());
 }
 
@@ -858,7 +712,7 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
                      dim3(P_NW * 64), ATTN_SMEM, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu,
                      pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
                      static_cast<const u32x4*>(k_ws), static_cast<const u32x4*>(v_ws), k_scale, order,
-                     rows_per_head);
+                     rows_per_head, max_seqlen);
   return int(hipGetLastError());
 }
 

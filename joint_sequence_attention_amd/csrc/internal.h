@@ -16,6 +16,12 @@ constexpr int kHeadDim = 128;
 constexpr int kPairs = kHeadDim / 2;
 constexpr int kKeyTile = 64;  // keys per packed workspace tile
 
+// Longest segment the attention kernels take.  A head's keys (and values) of
+// one segment occupy 256 bytes per key of the packed workspace and are read
+// through one buffer resource with 32-bit signed offsets; 2^22 keys (1 GiB)
+// keeps every offset and the resource's byte count below 2^31 in both modes.
+constexpr int32_t kMaxSeqlen = int32_t(1) << 22;
+
 // Rotary table for one call: per rotation pair p (dims 2p, 2p+1), the axis it
 // turns with (0 = t, 1 = h, 2 = w) and its angular frequency in float.
 struct RopeTable {

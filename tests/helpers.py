@@ -14,6 +14,17 @@ from joint_sequence_attention_amd import workloads as wl
 OUT_MAX_ABS = 1e-2
 OUT_MEAN_ABS = 1e-3
 LSE_MAX_ABS = 1e-3
+# Per (row, head): |out - out_ref|_2 <= OUT_REL_L2 * |out_ref|_2.  On long segments a row's output
+# is an average of many values and is small (|out| ~ sqrt(D / S), 0.03 at 130k keys), so the
+# absolute bars alone would pass an all-zero output there.  Expected relative error: the bf16
+# rounding of out (RMS about 2^-8 / sqrt(3) of each element), the bf16 rounding of P (the same
+# share of the weighted sum) and the fp16 score operands (logits off by ~2^-11 of their summed
+# magnitudes, a few 1e-3): together about 5e-3 per row; the bar is four times that.  A zeroed
+# output is off by 1, values taken from the wrong keys by about sqrt(2).
+OUT_REL_L2 = 2e-2
+# Query rows per attention workgroup: the sampled full-size checks take one row of every
+# (segment, 256-row query tile), with every head.
+WG_QUERY_ROWS = 256
 
 
 def say(msg: str):
@@ -105,17 +116,40 @@ class Case:
         rows.update(int(r) for r in rng.integers(0, self.N, size=n_random))
         return np.array(sorted(rows), dtype=np.int64)
 
+    def workgroup_rows(self, seed=0):
+        """One random row of every (segment, 256-row query tile), plus the edge rows of sample_rows."""
+        rng = np.random.default_rng(seed)
+        rows = set(int(r) for r in self.sample_rows(n_random=0, seed=seed))
+        for s in range(len(self.lens)):
+            a, b = int(self.cu[s]), int(self.cu[s + 1])
+            for t0 in range(a, b, WG_QUERY_ROWS):
+                rows.add(int(rng.integers(t0, min(b, t0 + WG_QUERY_ROWS))))
+        return np.array(sorted(rows), dtype=np.int64)
+
+
+def row_relative_error(out_gpu, out_ref):
+    """Per (row, head): |out_gpu - out_ref|_2 / |out_ref|_2 over the head dimension, [R, H]."""
+    num = np.sqrt(np.sum((out_gpu - out_ref) ** 2, axis=-1))
+    den = np.sqrt(np.sum(out_ref ** 2, axis=-1))
+    return num / np.maximum(den, 1e-30)
+
 
 def compare(out_gpu, lse_gpu, out_ref, lse_ref, out_max=OUT_MAX_ABS, out_mean=OUT_MEAN_ABS, lse_max=LSE_MAX_ABS,
-            label=""):
+            label="", out_rel=OUT_REL_L2):
+    """out_rel: the per-row relative bar (None for stress cases whose absolute bars are widened)."""
     err = np.abs(out_gpu - out_ref)
     lerr = np.abs(lse_gpu - lse_ref)
-    stats = dict(out_max=float(err.max()), out_mean=float(err.mean()), lse_max=float(lerr.max()))
-    say(f"{label} parity: out max {stats['out_max']:.3e} mean {stats['out_mean']:.3e} lse max {stats['lse_max']:.3e}")
+    rel = row_relative_error(out_gpu, out_ref) if out_gpu.size else np.zeros(1)
+    stats = dict(out_max=float(err.max()), out_mean=float(err.mean()), lse_max=float(lerr.max()),
+                 out_rel_max=float(rel.max()))
+    say(f"{label} parity: out max {stats['out_max']:.3e} mean {stats['out_mean']:.3e} lse max {stats['lse_max']:.3e} "
+        f"row-relative out max {stats['out_rel_max']:.3e}")
     assert np.all(np.isfinite(out_gpu)) and np.all(np.isfinite(lse_gpu))
     assert stats["out_max"] <= out_max, (label, stats, np.unravel_index(err.argmax(), err.shape))
     assert stats["out_mean"] <= out_mean, (label, stats)
     assert stats["lse_max"] <= lse_max, (label, stats, np.unravel_index(lerr.argmax(), lerr.shape))
+    if out_rel is not None:
+        assert stats["out_rel_max"] <= out_rel, (label, stats, np.unravel_index(rel.argmax(), rel.shape))
     return stats
 
 

@@ -240,3 +240,28 @@ def test_fp8_stage_argument_checks(L):
                                              _cfg(), 1 << 42, wsb, None, None) == H.H3ATTN_ERR_INVALID_ARG
     assert L.h3attn_varlen_kv_prologue_fp8(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, 64, 2, 64, 1, 64, _cfg(), 1 << 42,
                                            wsb, None) == H.H3ATTN_ERR_UNSUPPORTED
+
+
+def test_max_seqlen_limit(L):
+    # A segment's keys are addressed through 32-bit buffer offsets, 256 bytes per key: max_seqlen
+    # above 2^22 is refused in both modes and by every stage, before anything is launched.
+    N = (1 << 22) + 1
+    big = 1 << 44
+    for fp8 in (False, True):
+        wsb = (L.h3attn_varlen_fwd_fp8_workspace_size if fp8 else L.h3attn_varlen_fwd_workspace_size)(N, 1, 128, 1)
+        assert _fwd(L, N=N, Hh=1, ms=N, out=big, lse=2 * big, ws=4 * big, wsb=wsb, fp8=fp8) == \
+            H.H3ATTN_ERR_UNSUPPORTED
+        assert "2^22" in H.h3attn_last_error()
+        # 2^22 itself passes the size check and fails only later, on a NULL pointer
+        assert _fwd(L, N=N, Hh=1, ms=1 << 22, q=0, out=big, lse=2 * big, ws=4 * big, wsb=wsb, fp8=fp8) == \
+            H.H3ATTN_ERR_INVALID_ARG
+    wsb = L.h3attn_varlen_fwd_workspace_size(N, 1, 128, 1)
+    assert L.h3attn_varlen_kv_prologue(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, N, 1, 128, 1, N, _cfg(), 4 * big, wsb,
+                                       None) == H.H3ATTN_ERR_UNSUPPORTED
+    assert L.h3attn_varlen_attention(FAKE, FAKE * 4, FAKE * 5, big, 2 * big, N, 1, 128, 1, N, 0.0, _cfg(), 4 * big,
+                                     wsb, None) == H.H3ATTN_ERR_UNSUPPORTED
+    wsb8 = L.h3attn_varlen_fwd_fp8_workspace_size(N, 1, 128, 1)
+    assert L.h3attn_varlen_kv_prologue_fp8(FAKE, FAKE * 2, FAKE * 4, FAKE * 5, N, 1, 128, 1, N, _cfg(), 4 * big,
+                                           wsb8, None) == H.H3ATTN_ERR_UNSUPPORTED
+    assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, big, 2 * big, N, 1, 128, 1, N, 0.0, 0.0, _cfg(),
+                                         4 * big, wsb8, None, None) == H.H3ATTN_ERR_UNSUPPORTED
