@@ -2,70 +2,80 @@
 
 Test infrastructure only; see the package docstring.
 
-The vLLM-Omni "MiniMax-H3" recipe ("Attention Backends", the optional lossy
-optimizations of its datacenter-Blackwell backend) offers SAGE attention
-quantization for the long main DiT attention: Q and K in FP8 e4m3 with one
-scale per query token (query block size 1) and one scale per 16 keys (key
-block size 16), and P and V always in FP8.  It is lossy by design; the recipe
-asks to compare it against dense output before adopting it.
+What the page fixes.  The vLLM-Omni "MiniMax-H3" recipe, section "Attention
+Backends", describes two optional lossy optimizations of the long main DiT
+attention on its datacenter-Blackwell backend:
 
-The steps, in that order, with the readings taken where the page is silent:
+* SAGE attention quantization: Q and K in FP8 e4m3 with one scale per query
+  token (query block size 1) and one scale per 16 keys (key block size 16);
+  P and V are always FP8 in that kernel.
+* Skip-Softmax sparse attention with a direct threshold (0.05 in its
+  example): a low threshold skips only clearly negligible tiles of keys.
 
-1. Rotate Q and K (``rope``), then hold the rotated values in float32, the
-   precision device arithmetic uses (the position contract in "MiniMax H3 on
-   Moore Threads MUSA", "MUSA validation").  Quantization decisions are taken
-   on those float32 values.
-2. Block scales are powers of two: a block with largest magnitude a gets
-   2**e with e the smallest integer for which a * 2**-e <= 448 (the largest
-   finite e4m3 value), limited to [-127, 127]; a block of zeros gets 2**0.
-   Reading: the page gives block sizes, not the scale format; power-of-two
-   scales keep the scaling exact and match the hardware's 8-bit exponent
-   block scales.
-3. Q: one block per (token, head) row of 128 dims.  K: per head, blocks of 16
-   consecutive keys counted from the first key of each segment (the last block
-   of a segment may be shorter).  V: per head, blocks of 64 consecutive keys
-   from the segment start, all 128 dims (reading: the page says V is FP8 but
-   gives no V block size).  Each element is x8 = e4m3(x * 2**-e), rounded to
-   nearest even, and stands for x8 * 2**e.
-4. The softmax scale enters through the queries: each rotated query row is
-   multiplied by c = scale * log2(e) and held in float32 before it is
-   quantized, so q8 k8^T is the row's logits in base 2; z = (q8 k8^T) ln 2.
-   Reading: the page does not say where the scale enters; putting it into Q
-   before quantization gives a kernel base-2 logits straight from the matrix
-   core.  Exact softmax per row: m = max z, p = exp(z - m), l = sum p,
-   lse = m + ln l.
-5. P in FP8 (``quantize_p``): p8 = e4m3(p * 16) / 16, i.e. probabilities
-   relative to the row maximum, scaled by 2**4 so that values down to 2**-10
-   stay normal (reading: the page gives no P scale).  out = (p8 v8) / l.
-   A kernel that evaluates softmax online rounds its probabilities relative
-   to a running maximum instead, so its P rounding differs element by element;
-   both are draws of the same rounding noise, which the GPU tests bound.
+It gives nothing else: no scale format, no V or P block, no tile size, and
+no statement of where the softmax scale enters.  Those points are read here as
+follows, each for a reason that does not depend on any implementation.
 
-Skip-Softmax (optional, ``skip_threshold``).  The same recipe section offers
-a second lossy option, Skip-Softmax sparse attention with a direct threshold
-(0.05 there): tiles of keys whose probabilities are all below the threshold,
-relative to the running maximum, are left out.  The page names the knob, not
-the rule; the reading taken here, stated so that the result is a function of
-the logits alone:
+R1  Scale format.  One power-of-two scale 2^e per block, e the smallest
+    integer with amax * 2^-e <= 448 (the largest finite e4m3 value), limited
+    to [-127, 127]; a block of zeros takes 2^0.  Reason: plainest to check.
+    Scaling by a power of two is exact, so every quantized element is one
+    round-to-nearest-even of x * 2^-e that a reader can verify bit for bit;
+    of the power-of-two scales this is the finest that never saturates.
+R2  e4m3 flavour.  The OCP 8-bit floating-point E4M3 format the page names
+    ("fp8_e4m3": finite, largest 448, no infinities), round to nearest even
+    (the IEEE default).
+R3  Q blocks.  One block per (token, head) row of 128 rotated dims: the
+    page's query block size 1.
+R4  K blocks.  Per head, 16 consecutive keys counted from each segment's
+    first key (a segment's last block may be shorter): the page's key block
+    size 16.  A segment is one attention document, so no block spans two.
+R5  V blocks.  Per head, one scale per value channel (each of the 128 dims)
+    over all keys of the segment.  Reason: the page says V is FP8 and gives
+    no block.  The P.V product sums over keys, out_d = sum_j p_j v_jd / l, so
+    a scale that is constant along the keys of channel d factors out of that
+    sum exactly, whereas one that changed along the keys would not; per-channel
+    scaling of V is also the published SageAttention2 method's choice (Zhang
+    et al., "SageAttention2", FP8 quantization of P and V).
+R6  P.  Softmax itself is exact: the row maximum m, the probabilities
+    p = exp(z - m) and their sum l are taken in full precision, and P is
+    rounded to FP8 only where it enters the product with V.  Its scale comes
+    from R1 applied to P's bound known in advance: relative to the row
+    maximum every p lies in (0, 1], so e = -8 and p8 = e4m3(256 p) / 256.
+    lse = m + ln l and out = (p8 v8) / l.
+R7  Quantization precision.  Rotated Q and K are held in float32 (the
+    precision of device arithmetic: "MiniMax H3 on Moore Threads MUSA",
+    "MUSA validation") before they are scaled and rounded; V enters as given.
+R8  Where the softmax scale enters.  The logits are z = scale * (q8 . k8),
+    the scale applied to the product of the quantized operands: the page
+    quantizes Q and K themselves, and the scale belongs to the softmax, as in
+    the exact attention.
 
-* queries go in blocks of 32 rows and keys in tiles of 64 (the FP8 kernel's
-  units), both counted from the segment start, tiles in key order;
-* for each row, the running maximum before tile T is the largest logit of
-  the tiles before T (minus infinity for the first tile), whether or not
-  they were skipped;
-* tile T is skipped for a block when every valid row r of the block has
-  max_{j in T} z_rj < running_max_r + ln(threshold);
-* a skipped tile contributes nothing to that block's softmax: out and lse
-  are exact softmax over the keys of the tiles that are kept.
+Skip-Softmax readings.
 
-Rounding decisions near a midpoint.  A kernel rotates in its own fp32
-arithmetic, within 2^-22 (1 + |phi|)(|x0| + |x1|) of the exact rotation
-(angle rounding, sin/cos and the multiply-adds); this oracle's float32 values
-are within a quarter of that.  Where a midpoint of the e4m3 grid (or a
-power-of-two boundary of a block scale) lies inside that window, both
-roundings are correct.  ``error_scales`` reports, per row, how far such
-elements can move lse and out (first order, with margin), so that a test can
-tell a valid alternative rounding from a wrong one.
+S1  Decisions are per query row, and keys go in tiles of 64 counted from the
+    segment start, in key order.  Reason: the page speaks of tiles and gives
+    no size; 64 keys is four of the page's 16-key K blocks, so a tile never
+    splits a quantization block.  A per-row rule makes each row's result a
+    function of its own logits alone, which is the plainest to check.
+S2  Rule.  For row r, tile T is left out when max_{j in T} z_rj is below
+    M_r(T) + ln(threshold), where M_r(T) is the row's largest logit over the
+    tiles before T (minus infinity for the first tile, which is always kept).
+    A left-out tile's maximum lies below M_r(T), so M_r is also the running
+    maximum over the kept tiles.
+S3  Effect.  A left-out tile adds nothing to the row: out and lse are R6 over
+    the kept keys.
+S4  The rule sees the logits of R8, the scores of the quantized operands.
+
+Alternative roundings.  A kernel rotates in its own fp32 arithmetic, within
+2^-22 (1 + |phi|)(|x0| + |x1|) of the exact rotation (angle rounding, sin/cos
+and the multiply-adds); this oracle's float32 values are within a quarter of
+that.  Where a midpoint of the e4m3 grid (or a power-of-two boundary of a
+block scale) lies inside that window, both roundings are correct.
+``error_scales`` reports, per row, how far such elements can move lse and
+out (first order, with margin), and how far a skip decision next to the
+threshold can, so that a test can tell a valid alternative from a wrong one.
+V is not rotated: its quantization has no alternatives.
 """
 
 from __future__ import annotations
@@ -79,12 +89,10 @@ from .rope import rope
 E4M3_MAX = 448.0
 E4M3_MIN_NORMAL_EXP = -6          # smallest normal 2**-6
 E4M3_MANTISSA_BITS = 3
-Q_BLOCK = 1                        # query rows per scale
-K_BLOCK = 16                       # keys per scale
-V_BLOCK = 64                       # keys per scale (all dims)
-P_SCALE_LOG2 = 4                   # P is quantized as p * 2**4
-SKIP_QUERY_BLOCK = 32              # Skip-Softmax: query rows that decide together
-SKIP_KEY_TILE = 64                 # Skip-Softmax: keys skipped together
+Q_BLOCK = 1                        # R3: query rows per scale
+K_BLOCK = 16                       # R4: keys per scale
+P_SCALE_LOG2 = 8                   # R6: P is quantized as 256 p, p in (0, 1]
+SKIP_KEY_TILE = 64                 # S1: keys skipped together
 LN2 = math.log(2.0)
 
 
@@ -108,7 +116,7 @@ def round_e4m3(x) -> np.ndarray:
 
 
 def pow2_scale_exponent(amax) -> np.ndarray:
-    """Smallest integer e with amax * 2**-e <= 448, limited to [-127, 127]; 0 for amax == 0."""
+    """R1: smallest integer e with amax * 2**-e <= 448, limited to [-127, 127]; 0 for amax == 0."""
     amax = np.asarray(amax, dtype=np.float64)
     if np.any(amax < 0) or np.any(~np.isfinite(amax)):
         raise ValueError("amax must be finite and >= 0")
@@ -129,19 +137,33 @@ def quantize_block(x) -> np.ndarray:
 
 
 def quantize_rows(x) -> np.ndarray:
-    """Q-style quantization: one block per row of the last axis (any leading shape)."""
+    """R3, Q-style: one block per row of the last axis (any leading shape)."""
     x = np.asarray(x, dtype=np.float64)
     e = pow2_scale_exponent(np.abs(x).max(axis=-1))[..., None]
     return np.ldexp(round_e4m3(np.ldexp(x, -e)), e)
 
 
-def quantize_key_blocks(x, block) -> np.ndarray:
-    """Quantize x [S, D] in blocks of ``block`` consecutive rows from row 0 (last block may be short)."""
+def quantize_key_blocks(x, block=K_BLOCK) -> np.ndarray:
+    """R4: quantize x [S, D] in blocks of ``block`` consecutive rows from row 0 (last block may be short)."""
     x = np.asarray(x, dtype=np.float64)
     out = np.empty_like(x)
     for r0 in range(0, x.shape[0], block):
         out[r0:r0 + block] = quantize_block(x[r0:r0 + block])
     return out
+
+
+def quantize_channels(x) -> np.ndarray:
+    """R5: quantize x [S, D] with one scale per column (channel) over all S rows."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[0] == 0:
+        return x.copy()
+    e = pow2_scale_exponent(np.abs(x).max(axis=0))[None, :]
+    return np.ldexp(round_e4m3(np.ldexp(x, -e)), e)
+
+
+def quantize_p(p) -> np.ndarray:
+    """R6: probabilities relative to the row maximum, p in [0, 1], as e4m3(256 p) / 256."""
+    return np.ldexp(round_e4m3(np.ldexp(np.asarray(p, dtype=np.float64), P_SCALE_LOG2)), -P_SCALE_LOG2)
 
 
 ROTATION_ERROR = 2.0 ** -22          # fp32 rotation error coefficient (see the module docstring)
@@ -168,31 +190,39 @@ def rotation_error_bound(x, pos, theta=10000.0, dims=(32, 48, 48)) -> np.ndarray
     return out
 
 
-def quantize_block_margin(x, w):
-    """Quantize one block, and bound how much a rounding within +-w of each value could differ.
+def quantize_blocks_margin(xb, wb):
+    """Quantize blocks, and bound how much a rounding within +-w of each value could differ.
 
-    Returns (values the block stands for, change): change is 0 where every
-    value within +-w rounds the same way, else the largest move the other
-    rounding makes (one e4m3 step; for the whole block when its scale itself
-    could differ).
+    xb, wb: float64 [n_blocks, m], one block per row.  Returns (values the
+    blocks stand for, change), both [n_blocks, m]: change is 0 where every value
+    within +-w rounds the same way, else the largest move another valid
+    rounding makes.  Another evaluation may also find the block's largest
+    magnitude anywhere within +-wmax of this one's, and so a neighbouring
+    power-of-two scale where that crosses a boundary; each possible scale's
+    roundings of x - w, x and x + w count.  (A power of two leaves the e4m3
+    rounding of normal values alone: a scale change moves only values in or
+    near the subnormal range.)
     """
-    x = np.asarray(x, dtype=np.float64)
-    w = np.asarray(w, dtype=np.float64)
-    a = float(np.abs(x).max()) if x.size else 0.0
-    wmax = float(w.max()) if w.size else 0.0
-    e = int(pow2_scale_exponent(a))
-    s = np.ldexp(x, -e)
-    r = round_e4m3(s)
-    q = np.ldexp(r, e)
-    if int(pow2_scale_exponent(max(a - wmax, 0.0))) != int(pow2_scale_exponent(a + wmax)):
-        # the block scale may be 2^(e-1) or 2^(e+1): every value may move by a step at the coarser scale
-        change = np.abs(x) * 2.0 ** -3 + np.ldexp(1.0, e + 1 - 9)
-        return q, change
-    ws = np.ldexp(w, -e)
-    lo = round_e4m3(s - ws)
-    hi = round_e4m3(s + ws)
-    change = np.ldexp(np.maximum(np.abs(lo - r), np.abs(hi - r)), e)
+    xb = np.asarray(xb, dtype=np.float64)
+    wb = np.asarray(wb, dtype=np.float64)
+    a = np.abs(xb).max(axis=1) if xb.shape[1] else np.zeros(xb.shape[0])
+    wmax = wb.max(axis=1) if xb.shape[1] else np.zeros(xb.shape[0])
+    e = pow2_scale_exponent(a)[:, None]
+    q = np.ldexp(round_e4m3(np.ldexp(xb, -e)), e)
+    change = np.zeros_like(xb)
+    for e_alt in (pow2_scale_exponent(np.maximum(a - wmax, 0.0))[:, None], e,
+                  pow2_scale_exponent(a + wmax)[:, None]):
+        for sgn in (-1.0, 0.0, 1.0):
+            s_alt = np.clip(np.ldexp(xb + sgn * wb, -e_alt), -463.0, 463.0)
+            change = np.maximum(change, np.abs(np.ldexp(round_e4m3(s_alt), e_alt) - q))
     return q, change
+
+
+def quantize_block_margin(x, w):
+    """One block (any shape) through quantize_blocks_margin."""
+    x = np.asarray(x, dtype=np.float64)
+    q, change = quantize_blocks_margin(x.reshape(1, -1), np.asarray(w, dtype=np.float64).reshape(1, -1))
+    return q.reshape(x.shape), change.reshape(x.shape)
 
 
 def _to_f32(x):
@@ -200,36 +230,147 @@ def _to_f32(x):
 
 
 def _quantized_segment_kv(kr_seg, kw_seg, v_seg):
-    """Per-head K (16-key blocks, with rounding margins) and V (64-key blocks) of one segment, [S, H, D] each."""
+    """Per head: K in 16-key blocks with rounding margins (R4), V per channel over the segment (R5)."""
+    S, H, D = kr_seg.shape
+    nb = (S + K_BLOCK - 1) // K_BLOCK
+    pad = nb * K_BLOCK - S                 # zero rows: they change no block's largest magnitude
     kq = np.empty_like(kr_seg)
     kc = np.empty_like(kr_seg)
     vq = np.empty_like(v_seg)
-    for h in range(kr_seg.shape[1]):
-        for r0 in range(0, kr_seg.shape[0], K_BLOCK):
-            kq[r0:r0 + K_BLOCK, h], kc[r0:r0 + K_BLOCK, h] = quantize_block_margin(kr_seg[r0:r0 + K_BLOCK, h],
-                                                                                 kw_seg[r0:r0 + K_BLOCK, h])
-        vq[:, h, :] = quantize_key_blocks(v_seg[:, h, :], V_BLOCK)
+    for h in range(H):
+        xb = np.concatenate([kr_seg[:, h], np.zeros((pad, D))]).reshape(nb, K_BLOCK * D)
+        wb = np.concatenate([kw_seg[:, h], np.zeros((pad, D))]).reshape(nb, K_BLOCK * D)
+        q, c = quantize_blocks_margin(xb, wb)
+        kq[:, h] = q.reshape(nb * K_BLOCK, D)[:S]
+        kc[:, h] = c.reshape(nb * K_BLOCK, D)[:S]
+        vq[:, h, :] = quantize_channels(v_seg[:, h, :])
     return kq, kc, vq
 
 
-def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None, keep=None, amb=None, tile=64):
-    """One head of one segment for a set of query rows.
+def tile_maxima(m, tile=SKIP_KEY_TILE):
+    """Per row, the largest entry of each run of ``tile`` columns (the last run may be short): [R, n_tiles]."""
+    R, S = m.shape
+    full = S // tile
+    parts = [m[:, :full * tile].reshape(R, full, tile).max(axis=2)] if full else []
+    if S > full * tile:
+        parts.append(m[:, full * tile:].max(axis=1, keepdims=True))
+    return np.concatenate(parts, axis=1) if parts else np.zeros((R, 0))
+
+
+def skip_decisions(z, threshold, tile=SKIP_KEY_TILE, delta=None):
+    """S1-S2 for a set of rows: z float64 [R, S] (natural-unit logits) -> (skip, ambiguous), bool [R, n_tiles].
+
+    delta: float64 [R, n_tiles], how far evaluation error can move each logit of each tile (None:
+    0).  A decision is ambiguous when moving every tile's largest logit within its error could
+    change it: the running maximum then lies between the largest of the earlier tiles' maxima
+    moved down and the largest moved up.
+    """
+    R, S = z.shape
+    n_tiles = (S + tile - 1) // tile
+    skip = np.zeros((R, n_tiles), dtype=bool)
+    amb = np.zeros((R, n_tiles), dtype=bool)
+    if not threshold or threshold <= 0 or R == 0:
+        return skip, amb
+    ln_thr = math.log(threshold)
+    d = np.zeros((R, n_tiles)) if delta is None else np.asarray(delta, dtype=np.float64)
+    tm = tile_maxima(z, tile)
+
+    def before(x):
+        """Per tile, the largest of x over the earlier tiles (-inf for the first)."""
+        return np.maximum.accumulate(np.concatenate([np.full((R, 1), -np.inf), x[:, :-1]], axis=1), axis=1)
+
+    margin = before(tm) + ln_thr - tm                  # > 0: the row leaves the tile out
+    skip = margin > 0
+    lo = before(tm - d) + ln_thr - (tm + d)
+    hi = before(tm + d) + ln_thr - (tm - d)
+    amb = (lo <= 0) & (hi > 0)
+    return skip, amb
+
+
+def tile_logit_errors(q8, qc, k8, kc, scale, tile=SKIP_KEY_TILE):
+    """Per (row, key tile), how far a logit of the tile can move, float64 [R, n_tiles].
+
+    Two parts: fp32 evaluation of the 128 products, at most 2^-14 of their summed magnitudes,
+    bounded here by |scale| |q8_r|_2 |k8_j|_2 (Cauchy-Schwarz) with the tile's largest key norm;
+    and alternative roundings next to an e4m3 midpoint (qc, kc: how far each element may move),
+    |scale| sum_d (|q8_rd| kc_jd + qc_rd |k8_jd|), taken over the tile's keys.  Only keys and rows
+    that have an alternative enter the second part.
+    """
+    R, S = q8.shape[0], k8.shape[0]
+    sc = abs(scale)
+    knorm = np.sqrt((k8 * k8).sum(axis=1))
+    kmax = tile_maxima(knorm[None, :], tile)[0]
+    err = 2.0 ** -14 * sc * np.sqrt((q8 * q8).sum(axis=1))[:, None] * kmax[None, :]
+    jk = np.nonzero(kc.any(axis=1))[0]                 # keys with an alternative, ascending
+    if len(jk):
+        m = (np.abs(q8) @ kc[jk].T) * sc               # [R, len(jk)]
+        t_of = jk // tile
+        starts = np.concatenate([[0], np.nonzero(np.diff(t_of))[0] + 1])
+        err[:, t_of[starts]] += np.maximum.reduceat(m, starts, axis=1)
+    rq = np.nonzero(qc.any(axis=1))[0]
+    if len(rq):
+        err[rq] += tile_maxima((qc[rq] @ np.abs(k8).T) * sc, tile)
+    return err
+
+
+def skip_counts(q, k, cu_seqlens, pos, threshold, *, theta=10000.0, dims=(32, 48, 48), scale=None,
+                row_block=512):
+    """S1-S2 over every row: (left out, ambiguous), int64 [H, N]: per (head, row) the key tiles the
+    rule leaves out and the decisions among them that an evaluation error could flip.
+
+    The same quantized operands, rule and error bounds as ``sage_attention_rows``, without the
+    outputs.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    pos = np.asarray(pos, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    left = np.zeros((H, N), dtype=np.int64)
+    amb_n = np.zeros((H, N), dtype=np.int64)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            continue
+        k_seg = np.asarray(k[a:b], dtype=np.float64)
+        kr = _to_f32(rope(k_seg, pos[a:b], theta, dims))
+        kw = 2.0 * rotation_error_bound(k_seg, pos[a:b], theta, dims)
+        kq, kc, _ = _quantized_segment_kv(kr, kw, np.zeros_like(kr))
+        for r0 in range(a, b, row_block):
+            r1 = min(b, r0 + row_block)
+            q_rows = np.asarray(q[r0:r1], dtype=np.float64)
+            qr = _to_f32(rope(q_rows, pos[r0:r1], theta, dims))
+            qw = 2.0 * rotation_error_bound(q_rows, pos[r0:r1], theta, dims)
+            qq, qc = quantize_blocks_margin(qr.reshape(-1, D), qw.reshape(-1, D))
+            qq, qc = qq.reshape(qr.shape), qc.reshape(qr.shape)
+            for h in range(H):
+                z = (qq[:, h] @ kq[:, h].T) * scale
+                err = tile_logit_errors(qq[:, h], qc[:, h], kq[:, h], kc[:, h], scale)
+                sk, am = skip_decisions(z, threshold, SKIP_KEY_TILE, err)
+                left[h, r0:r1] = sk.sum(axis=1)
+                amb_n[h, r0:r1] = am.sum(axis=1)
+    return left, amb_n
+
+
+def _segment_head(q8, k8, v8, scale, quantize, qc=None, kc=None, keep=None, amb=None, tile=SKIP_KEY_TILE):
+    """One head of one segment for a set of query rows (R6, R8).
 
     keep: bool [R, S], the keys that count (all when None).  amb: bool [R, n_tiles], tiles whose
-    skip decision could go either way for the row's block (their effect is added to the error
-    scales).
+    skip decision could go either way for the row (their effect is added to the error scales).
     """
     z = (q8 @ k8.T) * scale
     zk = z if keep is None else np.where(keep, z, -np.inf)
     m = zk.max(axis=1, keepdims=True)
     p = np.exp(zk - m)
     l = p.sum(axis=1, keepdims=True)
-    pw = np.ldexp(round_e4m3(np.ldexp(p, P_SCALE_LOG2)), -P_SCALE_LOG2) if quantize_p else p
+    pw = quantize_p(p) if quantize else p
     out = (pw @ v8) / l
     lse = m[:, 0] + np.log(l[:, 0])
     # Spread of the P rounding: each probability moves by at most half an e4m3 ulp, 2^-4 of
-    # itself, or half the subnormal step, 2^-14 in these units; a rounding error spread evenly
-    # over that interval has standard deviation (bound) / sqrt(3).
+    # itself, or half the subnormal step, 2^-10 / 256; a rounding error spread evenly over that
+    # interval has standard deviation (bound) / sqrt(3).
     e = np.where(p > 0, np.maximum(p * 2.0 ** -4, 2.0 ** -(10 + P_SCALE_LOG2)), 0.0)
     sigma = np.sqrt(((e * e) @ (v8 * v8)) / 3.0) / l
     # Largest sum of absolute products behind one logit of the row: the scale of
@@ -267,34 +408,6 @@ def _segment_head(q8, k8, v8, scale, quantize_p, qc=None, kc=None, keep=None, am
     return out, lse, (sigma, zabs, lse_flip, out_flip)
 
 
-def skip_decisions(z, valid, threshold, tile=64, delta=None):
-    """Skip-Softmax decisions for one query block.
-
-    z: float64 [R, S] logits of the block's rows (natural units); valid: bool [R], the rows that
-    exist.  Returns (skip bool [n_tiles], ambiguous bool [n_tiles]).  A decision is ambiguous
-    when moving each row's logits by up to delta [R] (its evaluation error) could change it.
-    """
-    R, S = z.shape
-    n_tiles = (S + tile - 1) // tile
-    skip = np.zeros(n_tiles, dtype=bool)
-    amb = np.zeros(n_tiles, dtype=bool)
-    if not threshold or threshold <= 0 or not valid.any():
-        return skip, amb
-    ln_thr = math.log(threshold)
-    zv = z[valid]
-    d = np.zeros(zv.shape[0]) if delta is None else np.asarray(delta)[valid]
-    running = np.full(zv.shape[0], -np.inf)
-    for t in range(n_tiles):
-        tm = zv[:, t * tile:min(S, (t + 1) * tile)].max(axis=1)
-        margin = running + ln_thr - tm           # > 0: this row lets the tile go
-        skip[t] = bool(np.all(margin > 0))
-        could_skip = bool(np.all(margin > -2 * d))
-        could_keep = bool(np.any(margin < 2 * d))
-        amb[t] = could_skip and could_keep
-        running = np.maximum(running, tm)
-    return skip, amb
-
-
 def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, theta=10000.0, dims=(32, 48, 48),
                         scale=None, quantize_p=True, error_scales=False, skip_threshold=None):
     """Block-quantized FP8 attention for selected query rows (all rows when ``rows`` is None).
@@ -307,13 +420,12 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     scale * sum_i |q8_i k8_i| over its keys, float64 [len(heads), R]; and
     "lse_flip" [len(heads), R] and "out_flip" [R, len(heads), D], how far
     alternative roundings next to a midpoint (and skip decisions next to the
-    threshold) can move lse and out; "skipped" [len(heads), R], the share of
-    the row's key tiles left out, and "skip_ambiguous" [len(heads), R], how
-    many of its block's decisions could go either way.
+    threshold) can move lse and out; "skipped" [len(heads), R], the row's key
+    tiles left out, "tiles" [R], its segment's key tiles, and
+    "skip_ambiguous" [len(heads), R], how many of the row's decisions could go
+    either way.
 
-    skip_threshold: apply the Skip-Softmax rule above (None or 0: every tile
-    counts).  Each requested row's whole 32-row block is evaluated, since the
-    decision belongs to the block.
+    skip_threshold: apply the Skip-Softmax rule S1-S3 (None or 0: every tile counts).
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -329,16 +441,17 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
     rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    c = scale / LN2                     # base-2 logit coefficient, folded into the queries
     seg_of = np.searchsorted(cu, rows, side="right") - 1
-    out = np.zeros((len(rows), len(heads), D), dtype=np.float64)
-    lse = np.zeros((len(heads), len(rows)), dtype=np.float64)
-    sig = np.zeros((len(rows), len(heads), D), dtype=np.float64)
-    zabs = np.zeros((len(heads), len(rows)), dtype=np.float64)
-    lflip = np.zeros((len(heads), len(rows)), dtype=np.float64)
-    oflip = np.zeros((len(rows), len(heads), D), dtype=np.float64)
-    skipped = np.zeros((len(heads), len(rows)), dtype=np.float64)
-    ambiguous = np.zeros((len(heads), len(rows)), dtype=np.int64)
+    R = len(rows)
+    out = np.zeros((R, len(heads), D), dtype=np.float64)
+    lse = np.zeros((len(heads), R), dtype=np.float64)
+    sig = np.zeros((R, len(heads), D), dtype=np.float64)
+    zabs = np.zeros((len(heads), R), dtype=np.float64)
+    lflip = np.zeros((len(heads), R), dtype=np.float64)
+    oflip = np.zeros((R, len(heads), D), dtype=np.float64)
+    skipped = np.zeros((len(heads), R), dtype=np.int64)
+    ambiguous = np.zeros((len(heads), R), dtype=np.int64)
+    tiles = np.zeros(R, dtype=np.int64)
     for s in np.unique(seg_of):
         a, b = int(cu[s]), int(cu[s + 1])
         sel = np.nonzero(seg_of == s)[0]
@@ -347,67 +460,39 @@ def sage_attention_rows(q, k, v, cu_seqlens, pos, rows=None, heads=None, *, thet
         kw = 2.0 * rotation_error_bound(k_seg, pos[a:b], theta, dims)
         vs = np.asarray(v[a:b][:, heads, :], dtype=np.float64)
         kq, kc, vq = _quantized_segment_kv(kr, kw, vs)
-        # rows to evaluate: the requested ones, or with skipping their whole 32-row blocks
-        want = rows[sel] - a
-        if skip_threshold:
-            blocks = np.unique(want // SKIP_QUERY_BLOCK)
-            ev = np.concatenate([np.arange(bq * SKIP_QUERY_BLOCK, min(b - a, (bq + 1) * SKIP_QUERY_BLOCK))
-                                 for bq in blocks])
-        else:
-            ev = want
-        q_rows = np.asarray(q[a + ev][:, heads, :], dtype=np.float64)
-        qr = _to_f32(_to_f32(rope(q_rows, pos[a + ev], theta, dims)) * c)
-        # the rotation window times c, plus the float32 roundings of c and of the product
-        qw = 2.0 * rotation_error_bound(q_rows, pos[a + ev], theta, dims) * abs(c) + np.abs(qr) * 2.0 ** -22
-        qq = np.empty_like(qr)
-        qc = np.empty_like(qr)
-        for i in range(qr.shape[0]):
-            for j in range(qr.shape[1]):
-                qq[i, j], qc[i, j] = quantize_block_margin(qr[i, j], qw[i, j])
-        pos_in_ev = {int(r): i for i, r in enumerate(ev)}
-        pick = np.array([pos_in_ev[int(r)] for r in want])
+        r_seg = rows[sel]
+        q_rows = np.asarray(q[r_seg][:, heads, :], dtype=np.float64)
+        qr = _to_f32(rope(q_rows, pos[r_seg], theta, dims))
+        qw = 2.0 * rotation_error_bound(q_rows, pos[r_seg], theta, dims)
+        qq, qc = quantize_blocks_margin(qr.reshape(-1, D), qw.reshape(-1, D))   # R3: one block per row
+        qq, qc = qq.reshape(qr.shape), qc.reshape(qr.shape)
         S_seg = b - a
-        n_tiles = (S_seg + SKIP_KEY_TILE - 1) // SKIP_KEY_TILE
+        tiles[sel] = (S_seg + SKIP_KEY_TILE - 1) // SKIP_KEY_TILE
         for j in range(len(heads)):
-            # 512-row chunks hold whole 32-row blocks: every block but a segment's last is full
-            for r0 in range(0, len(ev), 512):
+            for r0 in range(0, len(sel), 512):
                 part = slice(r0, r0 + 512)
+                qp, qcp = qq[part, j, :], qc[part, j, :]
                 keep = amb = None
                 if skip_threshold:
-                    qp, qcp = qq[part, j, :], qc[part, j, :]
-                    z = (qp @ kq[:, j, :].T) * LN2
-                    za = (np.abs(qp) @ np.abs(kq[:, j, :]).T).max(axis=1) * LN2
-                    dzmax = ((np.abs(qp) @ kc[:, j, :].T + qcp @ np.abs(kq[:, j, :]).T) * LN2).max(axis=1)
-                    delta = 2.0 ** -14 * za + dzmax
-                    evp = ev[part]
-                    keep = np.ones((len(evp), S_seg), dtype=bool)
-                    amb = np.zeros((len(evp), n_tiles), dtype=bool)
-                    for bq in np.unique(evp // SKIP_QUERY_BLOCK):
-                        in_b = (evp // SKIP_QUERY_BLOCK) == bq
-                        sk, am = skip_decisions(z[in_b], np.ones(int(in_b.sum()), dtype=bool), skip_threshold,
-                                                SKIP_KEY_TILE, delta[in_b])
-                        keys_off = np.repeat(sk, SKIP_KEY_TILE)[:S_seg]
-                        keep[np.ix_(in_b, keys_off)] = False
-                        amb[in_b] = am
+                    z = (qp @ kq[:, j, :].T) * scale
+                    err = tile_logit_errors(qp, qcp, kq[:, j, :], kc[:, j, :], scale)
+                    sk, amb = skip_decisions(z, skip_threshold, SKIP_KEY_TILE, err)
+                    keep = ~np.repeat(sk, SKIP_KEY_TILE, axis=1)[:, :S_seg]
                     del z
-                o, l, (sg, za2, lf, of) = _segment_head(
-                    qq[part, j, :], kq[:, j, :], vq[:, j, :], LN2, quantize_p, qc[part, j, :], kc[:, j, :], keep,
-                    amb, SKIP_KEY_TILE)
-                idx = np.arange(len(ev))[part]
-                sel_here = np.nonzero(np.isin(pick, idx))[0]
-                loc = pick[sel_here] - r0
-                out[sel[sel_here], j, :] = o[loc]
-                lse[j, sel[sel_here]] = l[loc]
-                sig[sel[sel_here], j, :] = sg[loc]
-                zabs[j, sel[sel_here]] = za2[loc]
-                lflip[j, sel[sel_here]] = lf[loc]
-                oflip[sel[sel_here], j, :] = of[loc]
+                o, l, (sg, za2, lf, of) = _segment_head(qp, kq[:, j, :], vq[:, j, :], scale, quantize_p, qcp,
+                                                        kc[:, j, :], keep, amb, SKIP_KEY_TILE)
+                idx = sel[part]
+                out[idx, j, :] = o
+                lse[j, idx] = l
+                sig[idx, j, :] = sg
+                zabs[j, idx] = za2
+                lflip[j, idx] = lf
+                oflip[idx, j, :] = of
                 if keep is not None:
-                    kept_tiles = keep[loc][:, ::SKIP_KEY_TILE].sum(axis=1)
-                    skipped[j, sel[sel_here]] = 1.0 - kept_tiles / n_tiles
-                    ambiguous[j, sel[sel_here]] = amb[loc].sum(axis=1)
+                    skipped[j, idx] = sk.sum(axis=1)
+                    ambiguous[j, idx] = amb.sum(axis=1)
     scales = {"sigma": sig, "zabs": zabs, "lse_flip": lflip, "out_flip": oflip, "skipped": skipped,
-              "skip_ambiguous": ambiguous}
+              "tiles": tiles, "skip_ambiguous": ambiguous}
     return (out, lse, scales) if error_scales else (out, lse)
 
 

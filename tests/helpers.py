@@ -188,20 +188,28 @@ def ragged_segments():
 # Against the exact float64 oracle: the quality of the mode itself, on the
 # N(0, 1) workloads.  Rounding Q and K to 3-bit mantissas (relative error up to
 # 2^-4 each, standard deviation about 2^-4 / sqrt(3)) moves a logit by
-# sigma_z = c sqrt(2/3) 2^-4 |q * k|_2, about 0.05 for N(0, 1) rows.  A row
+# sigma_z = scale sqrt(2/3) 2^-4 |q * k|_2, about 0.05 for N(0, 1) rows.  A row
 # dominated by one key moves its lse by sigma_z: 5 sigma_z = 0.25.  Its output
 # moves by p (1 - p) sigma_z |v_a - v_b| for two competing keys, at most
 # 1/4 x 0.05 x 8 (4-sigma values of v) x 5 = 0.5; rounding V adds 2^-4 of
 # |v| on such rows.  Averaged over all outputs the error stays far smaller:
-# mean-abs 2e-2.  Wider inputs (the peaky case) are checked against the
-# quantized oracle only; their distance from exact softmax grows with the
-# logits and is reported.
+# mean-abs 2e-2.
+# Per (row, head) the relative L2 error |out - out_exact|_2 / |out_exact|_2 is
+# what stays meaningful on long rows, whose outputs are small averages: the
+# logit noise moves out by about sigma_z of itself, and the roundings of V and
+# P by about 2^-4 / sqrt(3) = 0.036 each, so sqrt(0.05^2 + 2 x 0.036^2) = 0.07;
+# the bar is four times that, 0.3 (measured on the float64 modes at 1344x768:
+# 0.053 mean, 0.068 largest of 200 row-heads).  A zeroed output is off by 1,
+# values taken from other keys by about 1.4.  Wider inputs (the peaky case) are
+# checked against the quantized oracle only; their distance from exact softmax
+# grows with the logits and is reported.
 FP8_SIGMAS = 6.0
 FP8_LSE_REL = 2.0 ** -16
 FP8_LSE_ABS = 1e-5
 FP8_EXACT_OUT_MAX = 0.5
 FP8_EXACT_OUT_MEAN = 2e-2
 FP8_EXACT_LSE_MAX = 0.25
+FP8_EXACT_REL = 0.3
 
 
 def compare_fp8(out_gpu, lse_gpu, out_sage, lse_sage, scales, out_exact, lse_exact, label="", exact_bars=True):
@@ -213,15 +221,17 @@ def compare_fp8(out_gpu, lse_gpu, out_sage, lse_sage, scales, out_exact, lse_exa
     lbound = FP8_LSE_REL * zabs + FP8_LSE_ABS + scales["lse_flip"]
     ex = np.abs(out_gpu - out_exact)
     lex = np.abs(lse_gpu - lse_exact)
+    rel = row_relative_error(out_gpu, out_exact)
     stats = dict(max_over_bound=float((d / bound).max()), rms_over_sigma=float(np.sqrt(np.mean((d / sigma) ** 2))),
                  lse_max=float(ld.max()), lse_max_over_bound=float((ld / lbound).max()),
                  rows_with_alternatives=int(np.count_nonzero(scales["lse_flip"])),
-                 exact_out_max=float(ex.max()), exact_out_mean=float(ex.mean()), exact_lse_max=float(lex.max()))
+                 exact_out_max=float(ex.max()), exact_out_mean=float(ex.mean()), exact_lse_max=float(lex.max()),
+                 exact_rel_max=float(rel.max()))
     say(f"{label} fp8: vs quantized oracle: max err/bound {stats['max_over_bound']:.3f}, rms err/sigma "
         f"{stats['rms_over_sigma']:.3f}, lse max {stats['lse_max']:.2e} (max err/bound {stats['lse_max_over_bound']:.3f}, "
         f"rows with alternative roundings {stats['rows_with_alternatives']}); "
         f"vs exact: out max {stats['exact_out_max']:.3e} mean {stats['exact_out_mean']:.3e} lse max "
-        f"{stats['exact_lse_max']:.3e}")
+        f"{stats['exact_lse_max']:.3e} row-relative max {stats['exact_rel_max']:.3e}")
     assert np.all(np.isfinite(out_gpu)) and np.all(np.isfinite(lse_gpu))
     assert stats["max_over_bound"] <= 1.0, (label, stats, np.unravel_index((d / bound).argmax(), d.shape))
     assert stats["lse_max_over_bound"] <= 1.0, (label, stats, np.unravel_index((ld / lbound).argmax(), ld.shape))
@@ -229,4 +239,5 @@ def compare_fp8(out_gpu, lse_gpu, out_sage, lse_sage, scales, out_exact, lse_exa
         assert stats["exact_out_max"] <= FP8_EXACT_OUT_MAX, (label, stats)
         assert stats["exact_out_mean"] <= FP8_EXACT_OUT_MEAN, (label, stats)
         assert stats["exact_lse_max"] <= FP8_EXACT_LSE_MAX, (label, stats)
+        assert stats["exact_rel_max"] <= FP8_EXACT_REL, (label, stats, np.unravel_index(rel.argmax(), rel.shape))
     return stats

@@ -105,33 +105,74 @@ def test_key_blocks_start_at_row_zero_and_are_independent():
     assert np.array_equal(got[32:], sage.quantize_block(x[32:]))        # the short last block stands alone
 
 
-C_DEFAULT = 1.0 / math.sqrt(D) / math.log(2.0)     # the base-2 logit coefficient at the default scale
+def _torch_e4m3(x):
+    """Round to e4m3 with torch's float8_e4m3fn cast: an independent rounding routine."""
+    x = np.asarray(x, dtype=np.float64)
+    return torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
-def _exact_inputs(n, h, seed):
-    """Inputs that the block quantization leaves unchanged.
+def _torch_block(x):
+    """One power-of-two scaled block, the scale found by doubling (R1), rounded by torch."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    e = 0
+    if amax > 0:
+        e = -127
+        while amax * 2.0 ** -e > 448.0:
+            e += 1
+    return _torch_e4m3(x * 2.0 ** -e) * 2.0 ** e
 
-    k and v: e4m3 values whose every block holds 448.  q: e4m3 values / c, so that the scaled
-    rows c q that get quantized are e4m3 values again (up to float32 rounding, which rounds back
-    to them); each row holds 416, clear of the 448 boundary where such a rounding could move the
-    row's scale.
-    """
-    rng = np.random.default_rng(seed)
-    g = _e4m3_grid()
-    pick = lambda shape, top: g[rng.integers(0, top, shape)] * rng.choice([-1.0, 1.0], shape)
-    q, k, v = pick((n, h, D), 126), pick((n, h, D), 127), pick((n, h, D), 127)   # code 125 is 416
-    q[:, :, 0] = 416.0
-    for r0 in range(0, n, 16):
-        k[r0, :, 0] = 448.0
-    for r0 in range(0, n, 64):
-        v[r0, :, 0] = 448.0
-    return q / 64.0 / C_DEFAULT, k / 64.0, v     # scales 2^-6: still exact
+
+def _quantized_operands(q, k, v, cu, pos):
+    """Q, K, V as the readings quantize them, written out with torch's rounding and loops."""
+    f32 = lambda a: np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)  # noqa: E731
+    qr, kr = f32(oracle.rope(q, pos)), f32(oracle.rope(k, pos))
+    q8, k8, v8 = np.zeros_like(qr), np.zeros_like(kr), np.zeros_like(v)
+    N, H, _ = q.shape
+    for h in range(H):
+        for i in range(N):
+            q8[i, h] = _torch_block(qr[i, h])                                  # R3: one row
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            for j in range(a, b, 16):
+                k8[j:min(j + 16, b), h] = _torch_block(kr[j:min(j + 16, b), h])  # R4: 16 keys from the start
+            for d in range(D):
+                v8[a:b, h, d] = _torch_block(v[a:b, h, d])                      # R5: one channel, whole segment
+    return q8, k8, v8
+
+
+def test_sage_is_exact_attention_of_the_quantized_operands():
+    # R3-R5 and R8: with P unrounded, the mode is exact softmax attention (the pinned exact
+    # oracle) of the quantized operands, the softmax scale applied to their product.  The
+    # default scale 1/sqrt(128) is not a power of two, so a mode that folded the scale into Q
+    # before rounding it would differ.
+    rng = np.random.default_rng(7)
+    cu = np.array([0, 40, 40, 111])
+    n, h = 111, 2
+    q, k, v = (rng.standard_normal((n, h, D)).astype(np.float32).astype(np.float64) for _ in range(3))
+    pos = np.stack([rng.integers(0, 6, n), rng.integers(0, 9, n), rng.integers(0, 9, n)], axis=1).astype(float)
+    q8, k8, v8 = _quantized_operands(q, k, v, cu, pos)
+    zero = np.zeros_like(pos)
+    for scale in (None, 0.3):
+        out_s, lse_s = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, scale=scale)
+        out_e, lse_e = oracle.attention(q8, k8, v8, cu, zero, scale=scale)   # already rotated: position 0
+        assert np.max(np.abs(out_s - out_e)) <= 1e-13
+        assert np.max(np.abs(lse_s - lse_e)) <= 1e-12
 
 
 def test_sage_equals_exact_attention_when_quantization_is_exact():
+    # Operands that are e4m3 values already (every K block and V channel holds 448, every Q row
+    # 416): the mode returns exact attention to rounding.
+    rng = np.random.default_rng(8)
     n, h = 150, 2
-    q, k, v = _exact_inputs(n, h, 7)
-    pos = np.zeros((n, 3))                  # identity rotation
+    g = _e4m3_grid()
+    pick = lambda shape, top: g[rng.integers(0, top, shape)] * rng.choice([-1.0, 1.0], shape)  # noqa: E731
+    q, k, v = pick((n, h, D), 126), pick((n, h, D), 127), pick((n, h, D), 127)
+    q[:, :, 0] = 416.0
+    k[::16, :, 0] = 448.0
+    v[0, :, :] = 448.0
+    q, k = q / 256.0, k / 64.0
+    pos = np.zeros((n, 3))
     cu = np.array([0, n])
     out_s, lse_s = sage.sage_attention(q, k, v, cu, pos, quantize_p=False)
     out_e, lse_e = oracle.attention(q, k, v, cu, pos)
@@ -139,71 +180,118 @@ def test_sage_equals_exact_attention_when_quantization_is_exact():
     assert np.max(np.abs(lse_s - lse_e)) <= 1e-12 * np.max(np.abs(lse_e))
 
 
-def test_sage_p_rounding_stays_within_its_bound():
-    n, h = 150, 2
-    q, k, v = _exact_inputs(n, h, 8)
-    q = q / 8.0                              # softer scores: many probabilities well below the maximum
+def test_value_channels_scale_independently():
+    # R5: a power of two on one value channel scales that channel's output exactly and leaves
+    # every other channel bit for bit; a scale shared across channels would not.
+    rng = np.random.default_rng(11)
+    n, h = 90, 2
+    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
+    pos = np.zeros((n, 3))
+    cu = np.array([0, 30, n])
+    out, lse = sage.sage_attention(q, k, v, cu, pos)
+    v2 = v.copy()
+    v2[:, 1, 5] *= 2.0 ** 7
+    out2, lse2 = sage.sage_attention(q, k, v2, cu, pos)
+    assert np.array_equal(lse2, lse)
+    assert np.array_equal(out2[:, 1, 5], np.ldexp(out[:, 1, 5], 7))
+    other = np.ones((n, h, D), dtype=bool)
+    other[:, 1, 5] = False
+    assert np.array_equal(out2[other], out[other])
+
+
+def test_value_channel_scale_spans_its_segment():
+    # R5: one large value sets its channel's scale for the whole segment, and for nothing else.
+    # At scale 2^12 the channel's other values (|v| ~ 1) fall below e4m3's normal range and
+    # round to the subnormal grid, so most of them change.
+    rng = np.random.default_rng(12)
+    n = 130
+    v = rng.standard_normal((n, D))
+    base = sage.quantize_channels(v)
+    v2 = v.copy()
+    v2[77, 9] = 2.0 ** 20
+    got = sage.quantize_channels(v2)
+    assert np.array_equal(np.delete(got, 9, axis=1), np.delete(base, 9, axis=1))
+    assert np.count_nonzero(got[:, 9] != base[:, 9]) > n // 2
+    e = int(sage.pow2_scale_exponent(2.0 ** 20))
+    assert e == 12
+    assert np.array_equal(got[:, 9], _torch_e4m3(v2[:, 9] * 2.0 ** -e) * 2.0 ** e)
+
+
+def test_p_rounding_closed_forms():
+    # R6: p relative to the row maximum, rounded as e4m3(256 p) / 256.
+    cases = {1.0: 1.0, 0.3: 0.3125, 3 * 2.0 ** -14: 3 * 2.0 ** -14,   # 3 * 2^-6 is a normal e4m3 value
+             2.0 ** -17: 2.0 ** -17,                                  # 2^-9, the smallest subnormal
+             2.0 ** -18: 0.0,                                         # half of it: a tie, to even (zero)
+             3 * 2.0 ** -18: 2.0 ** -16,                              # 1.5 subnormal steps: to even (two)
+             1.0625 * 2.0 ** -3: 2.0 ** -3}                           # a midpoint, to the even mantissa
+    for p, want in cases.items():
+        assert float(sage.quantize_p(p)) == want, (p, sage.quantize_p(p), want)
+    # the scale is the R1 rule applied to P's bound: the smallest power of two that fits 1 under 448
+    assert int(sage.pow2_scale_exponent(1.0)) == -sage.P_SCALE_LOG2
+
+
+def test_p_rounding_enters_only_the_product():
+    # R6: with P rounded, out = (p8 v8) / l with l the sum of the unrounded probabilities; lse is
+    # untouched.  Built from the quantized operands and torch's rounding of 256 p.
+    rng = np.random.default_rng(13)
+    n, h = 70, 1
+    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
+    q *= 2.0
     pos = np.zeros((n, 3))
     cu = np.array([0, n])
+    q8, k8, v8 = _quantized_operands(q, k, v, cu, pos)
+    z = (q8[:, 0] @ k8[:, 0].T) / math.sqrt(D)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    l = p.sum(axis=1, keepdims=True)
+    want = (_torch_e4m3(256.0 * p) / 256.0 @ v8[:, 0]) / l
     out_p, lse_p = sage.sage_attention(q, k, v, cu, pos, quantize_p=True)
     out_u, lse_u = sage.sage_attention(q, k, v, cu, pos, quantize_p=False)
-    assert np.array_equal(lse_p, lse_u)                # the row sums use unrounded probabilities
-    z = (q[:, 0] @ k[:, 0].T) / math.sqrt(D)
+    assert np.max(np.abs(out_p[:, 0] - want)) <= 1e-13
+    assert np.array_equal(lse_p, lse_u)
+    assert np.max(np.abs(out_p - out_u)) > 0
+
+
+def test_sage_p_rounding_spread():
+    # The reported spread: per probability half an e4m3 ulp (2^-4 of itself) or half the
+    # subnormal step (2^-10 / 256), squared over 3, summed with v^2; the actual rounding error
+    # across all rows and dims is of that size.
+    rng = np.random.default_rng(14)
+    n, h = 150, 2
+    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
+    pos = np.zeros((n, 3))
+    cu = np.array([0, n])
+    out_p, _ = sage.sage_attention(q, k, v, cu, pos, quantize_p=True)
+    out_u, _, es = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, error_scales=True)
+    q8, k8, v8 = _quantized_operands(q, k, v, cu, pos)
+    z = (q8[:, 0] @ k8[:, 0].T) / math.sqrt(D)
     p = np.exp(z - z.max(axis=1, keepdims=True))
-    # per probability: half an e4m3 ulp relative, or half the subnormal step (2^-10 / 16) absolute
-    err_p = np.maximum(p * 2.0 ** -4, 2.0 ** -14)
-    bound = (err_p @ np.abs(v[:, 0])) / p.sum(axis=1, keepdims=True)
-    assert np.all(np.abs(out_p[:, 0] - out_u[:, 0]) <= bound * (1 + 1e-12))
-    assert np.max(np.abs(out_p - out_u)) > 0           # P rounding is really applied
-    # the reported spread: the same per-probability bound, squared over 3, summed with v^2
-    _, _, es = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, error_scales=True)
-    sig = es["sigma"]
-    want = np.sqrt((err_p ** 2 @ v[:, 0] ** 2) / 3.0) / p.sum(axis=1, keepdims=True)
-    assert np.allclose(sig[:, 0], want, rtol=1e-12, atol=0)
-    zabs = np.array([max(sum(abs(q[i, 0, d] * k[j, 0, d]) for d in range(D)) for j in range(n)) for i in range(0, n, 37)])
+    err_p = np.maximum(p * 2.0 ** -4, 2.0 ** -18)
+    want = np.sqrt((err_p ** 2 @ v8[:, 0] ** 2) / 3.0) / p.sum(axis=1, keepdims=True)
+    assert np.allclose(es["sigma"][:, 0], want, rtol=1e-12, atol=0)
+    zabs = np.array([max(sum(abs(q8[i, 0, d] * k8[j, 0, d]) for d in range(D)) for j in range(n))
+                     for i in range(0, n, 37)])
     assert np.allclose(es["zabs"][0, ::37], zabs / math.sqrt(D), rtol=1e-12, atol=0)
-    # and the actual rounding error, across all rows and dims, is of that size
-    ratio = np.abs(out_p - out_u) / sig
+    ratio = np.abs(out_p - out_u) / es["sigma"]
     assert np.sqrt(np.mean(ratio ** 2)) < 1.0 and ratio.max() < 6.0
 
 
-def _scaled_query(x, scale):
-    """The row that gets quantized: float32(float32(x) * scale * log2 e), element by element."""
-    c = scale / math.log(2.0)
-    return np.array([float(np.float32(float(np.float32(t)) * c)) for t in x.ravel()]).reshape(x.shape)
-
-
 def _brute_sage(q, k, v, cu, scale):
-    """Loops over segment, head and query row; quantization from the block definition, written out."""
+    """Loops over segment, head and query row; quantization from the block definitions, written out."""
     N, H, _ = q.shape
     out = np.zeros((N, H, D))
     lse = np.zeros((H, N))
-
-    def qblock(x):
-        amax = max(abs(t) for t in x.ravel())
-        e = 0
-        if amax > 0:
-            e = -127
-            while amax * 2.0 ** -e > 448.0:
-                e += 1
-        return np.array([float(sage.round_e4m3(t * 2.0 ** -e)) * 2.0 ** e for t in x.ravel()]).reshape(x.shape)
-
+    q8, k8, v8 = _quantized_operands(q, k, v, cu, np.zeros((N, 3)))
     for s in range(len(cu) - 1):
         a, b = cu[s], cu[s + 1]
-        if a == b:
-            continue
         for h in range(H):
-            kq = np.concatenate([qblock(k[j:min(j + 16, b), h]) for j in range(a, b, 16)])
-            vq = np.concatenate([qblock(v[j:min(j + 64, b), h]) for j in range(a, b, 64)])
             for i in range(a, b):
-                qq = qblock(_scaled_query(q[i, h], scale))           # base-2 logits come out of q8 k8
-                z = [sum(qq[d] * kq[j][d] for d in range(D)) * math.log(2.0) for j in range(b - a)]
+                z = [sum(q8[i, h, d] * k8[j, h, d] for d in range(D)) * scale for j in range(a, b)]
                 zm = max(z)
                 p = [math.exp(t - zm) for t in z]
                 tot = sum(p)
-                pq = [float(sage.round_e4m3(t * 16.0)) / 16.0 for t in p]
+                pq = [float(_torch_e4m3(256.0 * t)) / 256.0 for t in p]
                 for d in range(D):
-                    out[i, h, d] = sum(pq[j] * vq[j][d] for j in range(b - a)) / tot
+                    out[i, h, d] = sum(pq[j - a] * v8[j, h, d] for j in range(a, b)) / tot
                 lse[h, i] = zm + math.log(tot)
     return out, lse
 
@@ -212,8 +300,7 @@ def test_sage_matches_brute_force():
     rng = np.random.default_rng(9)
     cu = np.array([0, 5, 5, 75])            # an empty segment and one that spans several blocks
     n, h = 75, 2
-    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
-    q, k, v = (x.astype(np.float32).astype(np.float64) for x in (q, k, v))
+    q, k, v = (rng.standard_normal((n, h, D)).astype(np.float32).astype(np.float64) for _ in range(3))
     pos = np.zeros((n, 3))
     out, lse = sage.sage_attention(q, k, v, cu, pos)
     bo, bl = _brute_sage(q, k, v, cu, 1.0 / math.sqrt(D))
@@ -241,17 +328,6 @@ def test_sage_segment_isolation_and_row_independence():
     rows = np.array([0, 36, 37, 80, 106, 127])
     orow, lrow = sage.sage_attention_rows(q, k, v, cu, pos, rows)
     assert np.array_equal(orow, out[rows]) and np.array_equal(lrow, lse[:, rows])
-
-
-def test_sage_value_scaling_is_exact():
-    rng = np.random.default_rng(11)
-    n, h = 90, 1
-    q, k, v = (rng.standard_normal((n, h, D)) for _ in range(3))
-    pos = np.zeros((n, 3))
-    cu = np.array([0, n])
-    out, _ = sage.sage_attention(q, k, v, cu, pos)
-    out2, _ = sage.sage_attention(q, k, np.ldexp(v, 7), cu, pos)
-    assert np.array_equal(out2, np.ldexp(out, 7))
 
 
 def test_sage_close_to_exact_on_the_tiny_workload():
@@ -316,10 +392,12 @@ def test_quantize_block_margin():
     blk[1] = 1.0625
     q, change = sage.quantize_block_margin(blk, np.full(4, 1e-9))
     assert change[1] == 0.125 and change[0] == 0 and change[2] == 0
-    # a block maximum next to a scale boundary flags the whole block
-    blk[0] = 448.0 * (1 + 1e-12)
-    q, change = sage.quantize_block_margin(blk, np.full(4, 1e-6))
-    assert np.all(change > 0)
+    # a block maximum next to a scale boundary (scales 2^0 and 2^1 both possible): a power of two
+    # leaves normal values' roundings alone, so only the midpoint and a value in the subnormal
+    # range (5 * 2^-12: one subnormal step at scale 2^0, zero at 2^1) are flagged
+    blk = np.array([448.0 * (1 + 1e-12), 1.0625, 0.0, 5 * 2.0 ** -12, 3.0])
+    q, change = sage.quantize_block_margin(blk, np.full(5, 1e-6))
+    assert change.tolist() == [0.0, 0.125, 0.0, 2.0 ** -9, 0.0]
 
 
 # ---- Skip-Softmax rule -----------------------------------------------------------------------
@@ -327,7 +405,7 @@ def test_quantize_block_margin():
 
 def _skip_case(seed, n=200, h=1, qscale=3.0):
     """Local attention: q_i . k_j = a^2 sum_m cos((i - j) w_m) + noise peaks at i = j, so tiles
-    far after a block's own keys carry almost no weight."""
+    far from a row's own keys carry almost no weight."""
     rng = np.random.default_rng(seed)
     w = 0.5 * np.power(10.0, -np.arange(D // 2) / (D // 2))
     ang = np.arange(n)[:, None] * w[None, :]
@@ -359,71 +437,136 @@ def test_skip_drops_a_negligible_tile():
     v = rng.standard_normal((n, 1, D))
     pos = np.zeros((n, 3))
     out, lse, es = sage.sage_attention(q, k, v, np.array([0, n]), pos, skip_threshold=0.05, error_scales=True)
-    ref_o, ref_l = sage.sage_attention_rows(q[:, :, :], np.concatenate([k[:64], k[:64]]),
-                                            np.concatenate([v[:64], np.zeros_like(v[:64])]),
-                                            np.array([0, 64, 128]), pos, np.arange(64))
-    # rows 0..63 against a segment holding only tile 0: same quantization of tile 0's blocks
-    assert np.allclose(out[:64], ref_o, rtol=0, atol=1e-12) and np.allclose(lse[:, :64], ref_l, rtol=0, atol=1e-12)
-    assert np.all(es["skipped"] == 0.5)
+    # against each row alone with its segment cut to tile 0: K blocks of tile 0 are the same, and
+    # the value channels are quantized over the whole segment, so the cut keeps v's scale by
+    # carrying each channel's largest magnitude along in a zero-weight key (logit -inf)
+    assert np.all(es["skipped"] == 1) and np.all(es["tiles"] == 2)
+    z = (sage.quantize_rows(np.float32(q[:, 0]).astype(np.float64)) @
+         sage.quantize_key_blocks(np.float32(k[:, 0]).astype(np.float64)).T) / math.sqrt(D)
+    v8 = sage.quantize_channels(v[:, 0])
+    p = np.exp(z[:, :64] - z[:, :64].max(axis=1, keepdims=True))
+    l = p.sum(axis=1, keepdims=True)
+    ref_o = (sage.quantize_p(p) @ v8[:64]) / l
+    ref_l = z[:, :64].max(axis=1) + np.log(l[:, 0])
+    assert np.max(np.abs(out[:, 0] - ref_o)) <= 1e-12 and np.max(np.abs(lse[0] - ref_l)) <= 1e-12
 
 
-def _brute_skip(q8, k8, v8, scale, thr):
-    """Loops: per 32-row block, per 64-key tile in order, the rule written out; exact softmax."""
-    R, S = q8.shape[0], k8.shape[0]
-    z = [[sum(q8[i, d] * k8[j, d] for d in range(D)) * scale for j in range(S)] for i in range(R)]
-    keep = [[True] * S for _ in range(R)]
-    for b0 in range(0, R, 32):
-        rows = range(b0, min(R, b0 + 32))
-        running = {i: -math.inf for i in rows}
-        for t0 in range(0, S, 64):
-            tmax = {i: max(z[i][t0:t0 + 64]) for i in rows}
-            if all(tmax[i] < running[i] + math.log(thr) for i in rows):
-                for i in rows:
-                    for j in range(t0, min(S, t0 + 64)):
-                        keep[i][j] = False
-            for i in rows:
-                running[i] = max(running[i], tmax[i])
+def _brute_skip(z, v8, thr):
+    """Loops: per row, per 64-key tile in key order, the rule written out; exact softmax over the
+    kept keys, P unrounded."""
+    R, S = len(z), len(z[0])
     out = np.zeros((R, D))
     lse = np.zeros(R)
+    kept_tiles = []
     for i in range(R):
-        ks = [j for j in range(S) if keep[i][j]]
-        zm = max(z[i][j] for j in ks)
-        e = {j: math.exp(z[i][j] - zm) for j in ks}
+        running = -math.inf
+        keep = []
+        for t0 in range(0, S, 64):
+            tmax = max(z[i][t0:t0 + 64])
+            if not tmax < running + math.log(thr):
+                keep.extend(range(t0, min(S, t0 + 64)))
+            running = max(running, tmax)
+        kept_tiles.append(len(set(j // 64 for j in keep)))
+        zm = max(z[i][j] for j in keep)
+        e = {j: math.exp(z[i][j] - zm) for j in keep}
         tot = sum(e.values())
         for d in range(D):
-            out[i, d] = sum(e[j] * v8[j, d] for j in ks) / tot
+            out[i, d] = sum(e[j] * v8[j, d] for j in keep) / tot
         lse[i] = zm + math.log(tot)
-    return out, lse, keep
+    return out, lse, np.array(kept_tiles)
 
 
 def test_skip_matches_brute_force():
     q, k, v, pos, cu = _skip_case(22, n=230, qscale=3.0)
     out, lse, es = sage.sage_attention(q, k, v, cu, pos, quantize_p=False, skip_threshold=0.05, error_scales=True)
-    # the same quantized operands, through the brute-force rule
-    q8 = sage.quantize_rows(_scaled_query(q[:, 0], 1.0 / math.sqrt(D)))
-    k8 = sage.quantize_key_blocks(k[:, 0], 16)
-    v8 = sage.quantize_key_blocks(v[:, 0], 64)
-    bo, bl, keep = _brute_skip(q8, k8, v8, math.log(2.0), 0.05)
+    q8, k8, v8 = _quantized_operands(q, k, v, cu, pos)
+    z = ((q8[:, 0] @ k8[:, 0].T) / math.sqrt(D)).tolist()
+    bo, bl, kept = _brute_skip(z, v8[:, 0], 0.05)
     assert np.max(np.abs(out[:, 0] - bo)) <= 1e-12 and np.max(np.abs(lse[0] - bl)) <= 1e-12
-    share = 1.0 - np.array([sum(keep[i][::64]) for i in range(len(keep))]) / 4.0
-    assert np.allclose(es["skipped"][0], share)
-    assert share.max() > 0                  # the case really skips something
+    assert np.array_equal(es["skipped"][0], 4 - kept)
+    assert es["skipped"].max() > 0                  # the case really skips something
 
 
-def test_skip_is_monotone_in_the_threshold_and_decided_per_block():
+def test_skip_is_decided_per_row():
+    # S1: each row decides alone.  Pointing row 6's query at key 200 (tile 3) makes row 6 keep
+    # tile 3; row 5, in the same 32 rows (one decision block under a block-wise rule), keeps its
+    # decisions and its output bit for bit.
     q, k, v, pos, cu = _skip_case(23, n=230, qscale=3.0)
+    out, lse, es = sage.sage_attention(q, k, v, cu, pos, skip_threshold=0.05, error_scales=True)
+    q2 = q.copy()
+    q2[6] = 3.0 * k[200]
+    out2, lse2, es2 = sage.sage_attention(q2, k, v, cu, pos, skip_threshold=0.05, error_scales=True)
+    assert es["skipped"][0][5] > 0
+    assert es2["skipped"][0][6] != es["skipped"][0][6]
+    others = np.arange(230) != 6
+    assert np.array_equal(es2["skipped"][0][others], es["skipped"][0][others])
+    assert np.array_equal(out2[others], out[others]) and np.array_equal(lse2[:, others], lse[:, others])
+    # and a single row evaluated alone decides as it does among the others
+    o5, l5, e5 = sage.sage_attention_rows(q, k, v, cu, pos, np.array([5]), skip_threshold=0.05, error_scales=True)
+    assert np.array_equal(o5[0], out[5]) and e5["skipped"][0][0] == es["skipped"][0][5]
+
+
+def test_skip_first_tile_always_kept_and_monotone_in_the_threshold():
+    q, k, v, pos, cu = _skip_case(24, n=230, qscale=3.0)
     shares = []
-    for thr in (1e-6, 1e-3, 0.05, 0.3):
+    for thr in (1e-6, 1e-3, 0.05, 0.3, 0.99):
         _, _, es = sage.sage_attention(q, k, v, cu, pos, skip_threshold=thr, error_scales=True)
         shares.append(es["skipped"][0])
+        assert np.all(es["skipped"][0] <= es["tiles"] - 1)      # the first tile always counts
     for lo, hi in zip(shares, shares[1:]):
         assert np.all(hi >= lo)
-    # every row of a 32-row block shares the block's decisions
-    for b0 in range(0, 230, 32):
-        assert np.all(shares[2][b0:b0 + 32] == shares[2][b0])
-    # one row that needs tile 1 keeps it for its whole block: give row 5 a key of tile 1 that it
-    # matches strongly
-    k2 = k.copy()
-    k2[70, 0] = q[5, 0] * 3.0
-    _, _, es2 = sage.sage_attention(q, k2, v, cu, pos, skip_threshold=0.05, error_scales=True)
-    assert es2["skipped"][0][0] <= shares[2][0]
+
+
+def test_skip_decisions_closed_form():
+    # Two rows, three tiles: row 0's logits fall off tile by tile, row 1's rise.
+    z = np.array([[0.0] * 64 + [-3.5] * 64 + [-2.0] * 10,
+                  [0.0] * 64 + [1.0] * 64 + [-5.0] * 10])
+    skip, amb = sage.skip_decisions(z, 0.05)                 # ln 0.05 = -2.996
+    assert skip.tolist() == [[False, True, False], [False, False, True]]
+    assert not amb.any()
+    skip, amb = sage.skip_decisions(z, 0.05, delta=np.array([[0.3, 0.3, 0.3], [0.0, 0.0, 0.0]]))
+    # row 0: tile 1's margin 0 - 2.996 + 3.5 = 0.504 can move by 0.3 + 0.3 down to -0.096;
+    # tile 2's, -0.996, at most to -0.396: clear
+    assert amb.tolist() == [[False, True, False], [False, False, False]]
+    # the running maximum moves with the tile that sets it
+    skip, amb = sage.skip_decisions(z, 0.05, delta=np.array([[0.6, 0.0, 0.0], [0.0, 0.0, 0.0]]))
+    assert amb.tolist() == [[False, True, False], [False, False, False]]
+    skip, amb = sage.skip_decisions(z, 0.05, delta=np.array([[0.0, 0.5, 0.0], [0.0, 0.0, 0.0]]))
+    assert amb.tolist() == [[False, False, False], [False, False, False]]
+    # ... and not with an earlier tile far below it: row 1's tile 0 (maximum 0) with a wide error
+    # of 0.9 cannot reach tile 1's maximum 1.0, which sets the running maximum for tile 2
+    skip, amb = sage.skip_decisions(z, 0.05, delta=np.array([[0.0, 0.0, 0.0], [0.9, 0.0, 0.0]]))
+    assert amb.tolist() == [[False, False, False], [False, False, False]]
+
+
+def test_tile_logit_errors_bound_alternative_roundings():
+    # moving every element that has an alternative rounding by its full change moves each logit
+    # by no more than the per-tile error the oracle states
+    rng = np.random.default_rng(26)
+    q8 = sage.quantize_rows(rng.standard_normal((20, D)))
+    k8 = sage.quantize_key_blocks(rng.standard_normal((150, D)))
+    qc = np.where(rng.random(q8.shape) < 0.01, np.abs(q8) * 2.0 ** -3, 0.0)
+    kc = np.where(rng.random(k8.shape) < 0.01, np.abs(k8) * 2.0 ** -3, 0.0)
+    scale = 0.088
+    err = sage.tile_logit_errors(q8, qc, k8, kc, scale)
+    z = q8 @ k8.T * scale
+    for trial in range(20):
+        sq, sk = rng.choice([-1.0, 1.0], q8.shape), rng.choice([-1.0, 1.0], k8.shape)
+        z2 = (q8 + sq * qc) @ (k8 + sk * kc).T * scale
+        moved = np.abs(z2 - z)
+        for t in range(3):
+            # first order: the product of two moved elements is second order and far smaller
+            assert np.all(moved[:, 64 * t:64 * (t + 1)].max(axis=1) <= err[:, t] * (1 + 2.0 ** -3) + 1e-12)
+
+
+def test_skip_counts_match_the_per_row_evaluation():
+    # skip_counts (every row, no outputs) gives the same left-out and ambiguous counts as the full
+    # evaluation, on a local case with rotated positions and two segments
+    q, k, v, _, _ = _skip_case(25, n=300, h=2, qscale=3.0)
+    rng = np.random.default_rng(25)
+    pos = np.stack([rng.integers(0, 3, 300), rng.integers(0, 5, 300), rng.integers(0, 5, 300)], axis=1).astype(float)
+    cu = np.array([0, 170, 300])
+    _, _, es = sage.sage_attention(q, k, v, cu, pos, skip_threshold=0.05, error_scales=True)
+    left, amb = sage.skip_counts(q, k, cu, pos, 0.05, row_block=64)
+    assert np.array_equal(left, es["skipped"]) and np.array_equal(amb, es["skip_ambiguous"])
+    assert left.sum() > 0
