@@ -20,8 +20,8 @@ e4m3 Q/K/P/V with block scales), with its own roofline against the fp8 dense
 MFMA peak.  It is reported beside the bf16 metric, never in its place.
 fp8_mode.skip_softmax: the FP8 attention kernel with Skip-Softmax at threshold
 0.05, against the dense FP8 kernel, both on seeded inputs whose attention is
-local (workloads.local_qkv); the share of (32-row block, 64-key tile) pairs
-left out is the kernel's own count.  effective_tflops counts the dense FLOP.
+local (workloads.local_qkv); the share of (query row, 64-key tile) pairs left
+out is the kernel's own count.  effective_tflops counts the dense FLOP.
 """
 
 from __future__ import annotations
@@ -407,7 +407,8 @@ def main():
     print(f"[bench] fp8 mode: {fp8_ms_per_step:.3f} ms/step, attention kernel {fp8_attn_ms:.3f} ms -> "
           f"{fp8_achieved:.1f} TFLOP/s ({100 * fp8_achieved / PEAK_FP8_TFLOPS:.1f}% of fp8 peak)", file=sys.stderr,
           flush=True)
-    fp8 = {"mode": "lossy FP8 (SAGE-style e4m3 Q/K/P/V, block scales), h3attn_varlen_fwd_fp8",
+    fp8 = {"mode": "lossy FP8 (SAGE-style e4m3: Q per row, K per 16 keys, V per channel, P x 256; power-of-two "
+                   "scales), h3attn_varlen_fwd_fp8",
            "value": round(flop / (fp8_ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
            "ms_per_step": round(fp8_ms_per_step, 4), "dtype": "fp8 e4m3 operands, fp32 accumulate",
            "roofline": {"bound": "mfma", "achieved": round(fp8_achieved, 2), "peak": PEAK_FP8_TFLOPS,
@@ -440,7 +441,7 @@ def main():
     dense_ms, _ = time_fp8_attention(0.0)
     skip_ms, skip_share = time_fp8_attention(SKIP_THRESHOLD)
     print(f"[bench] skip-softmax {SKIP_THRESHOLD} on local-attention inputs: {skip_ms:.3f} ms vs dense fp8 "
-          f"{dense_ms:.3f} ms ({dense_ms / skip_ms:.3f}x), {100 * skip_share:.1f}% of (block, tile) pairs left out",
+          f"{dense_ms:.3f} ms ({dense_ms / skip_ms:.3f}x), {100 * skip_share:.1f}% of (row, tile) pairs left out",
           file=sys.stderr, flush=True)
     fp8["skip_softmax"] = {
         "threshold": SKIP_THRESHOLD,

@@ -186,30 +186,32 @@ h3attn_status h3attn_varlen_attention(const void* q, const int32_t* cu_seqlens, 
  * probabilities and values are FP8 as well.  The recipe marks it lossy and
  * asks for a comparison against dense output before use.
  *
- * Here: rotated queries and keys (fp32) are scaled per block by a power of
- * two (the smallest that brings the block's largest magnitude to <= 448) and
- * rounded to nearest e4m3; one block is a (token, head) row of q, or 16
- * consecutive keys of one head counted from its segment's first key.  Values
- * are scaled per 64 consecutive keys of one head and rounded likewise.
- * Probabilities enter the second contraction as e4m3 of p * 2^4 relative to
- * a running maximum; row sums and all accumulation are fp32; out is bf16 and
- * lse fp32 exactly as for h3attn_varlen_fwd, whose argument meanings, layout,
- * ownership and error rules apply unchanged.  Only the workspace differs:
- * it must hold h3attn_varlen_fwd_fp8_workspace_size bytes (256-byte aligned)
- * and its contents on return are unspecified.
+ * Here: every scale is a power of two, the smallest that brings its block's
+ * largest magnitude to <= 448, and every value is rounded to nearest e4m3
+ * (OCP E4M3).  Blocks: a (token, head) row of rotated q (fp32); 16
+ * consecutive rotated keys of one head counted from the segment's first key;
+ * one value channel (one of the 128 dims) of one head over all keys of the
+ * segment.  The logits are softmax_scale times the product of the quantized
+ * q and k.  Softmax itself is exact (fp32 running maximum and row sums of the
+ * unrounded probabilities); probabilities enter the product with V as
+ * e4m3(256 p) with p relative to a running maximum; all accumulation is fp32;
+ * out is bf16 and lse fp32 exactly as for h3attn_varlen_fwd, whose argument
+ * meanings, layout, ownership and error rules apply unchanged.  Only the
+ * workspace differs: it must hold h3attn_varlen_fwd_fp8_workspace_size bytes
+ * (256-byte aligned) and its contents on return are unspecified.
  *
  * Skip-Softmax (same recipe section: an optional lossy "sparse attention"
  * with a direct threshold, 0.05 there).  skip_threshold in [0, 1); 0 computes
- * every key.  Otherwise queries go in blocks of 32 rows and keys in tiles of
- * 64, both counted from the segment start; a block leaves a tile out when
- * every row of the block has its largest logit in the tile below
- * ln(skip_threshold) plus its largest logit over the earlier tiles, and out
- * and lse are then softmax over the kept tiles.  Whether to use it for a
- * given denoising step (the recipe keeps the early, high-noise steps dense)
- * is the caller's choice.  skip_stats: NULL, or device uint64[2] to which the
- * call adds the (block, tile) pairs it saw and those it left out (nothing
- * when skip_threshold is 0); the caller clears it.  Fails with INVALID_ARG
- * for a threshold outside [0, 1).
+ * every key.  Otherwise keys go in tiles of 64 counted from the segment
+ * start, and each query row decides alone: it leaves a tile out when its
+ * largest logit in the tile is below ln(skip_threshold) plus its largest
+ * logit over the earlier tiles (the first tile is always kept); out and lse
+ * are then softmax over the kept tiles.  Whether to use it for a given
+ * denoising step (the recipe keeps the early, high-noise steps dense) is the
+ * caller's choice.  skip_stats: NULL, or device uint64[2] to which the call
+ * adds the (row, tile) pairs its rows saw and those they left out (nothing
+ * when skip_threshold is 0); the caller clears it.  Fails with INVALID_ARG for
+ * a threshold outside [0, 1).
  * ------------------------------------------------------------------- */
 size_t h3attn_varlen_fwd_fp8_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs);
 

@@ -292,7 +292,7 @@ h3attn_status h3attn_varlen_kv_prologue_fp8(const void* k, const void* v, const 
     return hip_status(launch_kv_prologue_fp8(k, v, cu_seqlens, pos_thw, n_heads, n_seqs, max_seqlen, table,
                                              ws + wl.keys_offset, ws + wl.values_offset,
                                              reinterpret_cast<unsigned*>(ws + wl.kscale_offset),
-                                             reinterpret_cast<unsigned*>(ws + wl.vscale_offset),
+                                             reinterpret_cast<unsigned*>(ws + wl.vamax_offset),
                                              reinterpret_cast<int32_t*>(ws + wl.order_offset), rows, stream));
   } catch (...) {
     return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_kv_prologue_fp8");
@@ -328,7 +328,7 @@ h3attn_status h3attn_varlen_attention_fp8(const void* q, const int32_t* cu_seqle
     return hip_status(launch_attention_fp8(q, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, n_seqs, max_seqlen,
                                            scale, skip_threshold, table, ws + wl.keys_offset, ws + wl.values_offset,
                                            reinterpret_cast<const unsigned*>(ws + wl.kscale_offset),
-                                           reinterpret_cast<const unsigned*>(ws + wl.vscale_offset),
+                                           reinterpret_cast<const unsigned*>(ws + wl.vamax_offset),
                                            reinterpret_cast<const int32_t*>(ws + wl.order_offset), rows,
                                            reinterpret_cast<unsigned long long*>(skip_stats), stream));
   } catch (...) {

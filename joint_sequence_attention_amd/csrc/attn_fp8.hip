@@ -4,20 +4,33 @@
 // The mode: SAGE-style quantization of the long main DiT attention (vLLM-Omni
 // "MiniMax-H3" recipe, "Attention Backends"): queries and keys in FP8 e4m3
 // with one scale per query token and one scale per 16 keys, probabilities and
-// values in FP8 too.  The attention itself is the one the exact path computes
-// ("Day 0 Support for MiniMax-H3 on AMD Instinct GPUs", "The diffusion
-// transformer (DiT)"): every token of a packed segment attends to every token
-// of its segment, after the multi-axis rotation of queries and keys.
+// values in FP8 too, and optionally Skip-Softmax tile skipping.  The
+// attention itself is the one the exact path computes ("Day 0 Support for
+// MiniMax-H3 on AMD Instinct GPUs", "The diffusion transformer (DiT)"): every
+// token of a packed segment attends to every token of its segment, after the
+// multi-axis rotation of queries and keys.
 //
-// Two kernels:
-//   kv_prologue_fp8_kernel  rotates K, quantizes it in 16-key blocks and V in
-//                           64-key blocks (power-of-two scales), and packs
-//                           both into 64-key tiles, V transposed.  HBM-bound.
+// What is quantized how (the page gives only the block sizes):
+//   * every scale is a power of two 2^e, e the smallest integer that brings the
+//     block's largest magnitude to at most 448 (the largest finite e4m3 value);
+//   * Q: one block per (token, head) row of 128 rotated dims; K: 16 keys of one
+//     head counted from the segment's first key; V: one scale per value
+//     channel over all keys of the segment (a scale constant along the keys
+//     factors out of the sum over keys); P: the same rule applied to its bound
+//     1 relative to the row maximum, i.e. e4m3(256 p);
+//   * the softmax scale multiplies the product of the quantized Q and K.
+//
+// Kernels:
+//   fp8_clear_kernel        zeroes the per-channel value maxima.
+//   kv_prologue_fp8_kernel  rotates K, quantizes it in 16-key blocks and packs
+//                           it into 64-key tiles; takes each value channel's
+//                           largest magnitude over its segment (atomic max).
+//   v_quant_fp8_kernel      quantizes V with those channel scales and packs it,
+//                           transposed, into 64-key tiles.  Both HBM-bound.
 //   attn_fwd_fp8_kernel     one workgroup per (256-query tile, head, segment
 //                           rank), longest segments first; eight waves, 32
-//                           queries per wave; 64-key tiles
-//                           through LDS rings; both contractions on
-//                           v_mfma_scale_f32_32x32x64_f8f6f4.
+//                           queries per wave; 64-key tiles through LDS rings;
+//                           both contractions on v_mfma_scale_f32_32x32x64_f8f6f4.
 //
 // MFMA orientation.  As in the bf16 kernel, scores are computed transposed,
 // S^T = K Q^T: A = 32 keys x 64 dims (LDS), B = 64 dims x 32 queries
@@ -30,14 +43,14 @@
 // hardware pairs byte b of lane group g in A with byte b of lane group g in
 // B, so any order works as long as both sides use the same one.
 //
-// Scales.  Per query row: a power-of-two factor folded into the base-2 logit
-// coefficient.  Per 16 keys: the 8-bit exponent scale of the A operand (the
-// matrix core applies it; the scale of lanes L and L + 32 covers key L % 32).
-// Per 64 keys of V: the same, one value for all lanes.  Probabilities are
-// formed as p * 2^4 (the shift is folded into the running maximum) so that
-// values down to 2^-10 of the maximum stay normal e4m3; row sums add the
-// unrounded fp32 probabilities.
+// Scales.  The matrix core applies every block scale as an 8-bit exponent:
+// per query row the B scale of the score products (each lane carries its
+// row's), per 16 keys the A scale (the scale of lanes L and L + 32 covers key
+// L % 32), and per value channel the A scale of the value products (lane L of
+// value-dim block db carries channel 32 db + L % 32's).  So a score MFMA
+// returns q8 . k8 itself and a value MFMA sum_j p'_j v8_jd.
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 
@@ -55,8 +68,13 @@ constexpr int F8_BQ = 32 * F8_NW;        // 256 query rows per workgroup
 constexpr int F8_NS = 8;                 // slots per ring
 constexpr int F8_VBASE = F8_NS * F8_TILE_BYTES;
 constexpr size_t F8_SMEM = 2 * F8_NS * F8_TILE_BYTES;  // 128 KiB
-constexpr float P_SHIFT = 4.0f;          // probabilities are stored as p * 2^4
-constexpr float LAZY_SUM = 256.0f;       // largest row sum of a tile's scaled probabilities left unrescaled
+constexpr float P_SHIFT = 8.0f;          // probabilities are stored as p * 2^8, p relative to the row maximum
+constexpr float E4M3_TOP = 448.0f;       // largest finite e4m3 value
+// A stored probability p' = 2^(z - mm) with z the base-2 logit and mm the
+// running reference minus 8; it must not exceed 448, i.e. z - mm <= log2 448.
+// The reference is moved when that could fail; 8.75 < log2 448 = 8.807 leaves
+// room for the rounding of the exponent's argument.
+constexpr float P_ROOM_LOG2 = 8.75f;
 constexpr int E8M0_ONE = 127;            // 8-bit exponent scale of 2^0
 
 // LDS layouts, XOR-swizzled so that the 16-byte fragment reads of a wave hit
@@ -75,27 +93,35 @@ __device__ __forceinline__ int v8_key_byte(int kk) {
 }
 
 // ---------------------------------------------------------------------------
-// FP8 K/V prologue.  grid = (64-key tiles of the longest segment, segments,
-// heads), 256 threads.
+// Per-channel value maxima start at 0 (bit pattern of +0.0f).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_clear_kernel(unsigned* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 K/V prologue, pass 1.  grid = (64-key tiles of the longest segment,
+// segments, heads), 256 threads.
 // k_ws:   [H][rows][128] e4m3 rotated keys, rows past a segment's end zero.
-// v_ws:   [H][rows/64][128][64] e4m3 values, transposed per tile, keys in the
-//         order v8_key_byte gives.
 // k_sc:   [H][rows/64] one word per tile: byte i = 8-bit exponent scale of
 //         keys 16i .. 16i+15.
-// v_sc:   [H][rows/64] one word per tile: the exponent scale of its values.
+// v_amax: [H][n_seqs][128] per value channel, the largest magnitude over the
+//         segment (float bit patterns, which order like the values since they
+//         are >= 0); raised here with atomic max from 0.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __restrict__ k,
                                                               const u32x4* __restrict__ v,
                                                               const int32_t* __restrict__ cu,
                                                               const float* __restrict__ pos, int32_t n_heads,
                                                               RopeTable tab, u32x2* __restrict__ k_ws,
-                                                              unsigned* __restrict__ v_ws,
-                                                              unsigned* __restrict__ k_sc, unsigned* __restrict__ v_sc,
+                                                              unsigned* __restrict__ k_sc,
+                                                              unsigned* __restrict__ v_amax,
                                                               int32_t* __restrict__ order, int64_t rows_per_head,
                                                               int32_t max_seqlen) {
   __shared__ float s_omega[kPairs];
   __shared__ int s_axis[kPairs];
-  __shared__ float s_red[4][5];
+  __shared__ float s_red[4][4];
   const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   if (tile == 0 && h == 0) write_segment_rank(cu, int(gridDim.y), s, order);  // before any early exit
   const int32_t seg_a = cu[s];
@@ -110,7 +136,7 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
   // Keys: 1024 chunks of 8 dims, 4 per thread; chunk i of the thread is key
   // (tid >> 4) + 16 i, dims 8 (tid & 15) ..; so chunk i lies in 16-key block i.
   float kf[4][8];
-  float amax[5];
+  float amax[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 4) + 16 * i, cc = tid & 15;
@@ -129,44 +155,57 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
     amax[i] = m;
   }
 
-  // Values: thread owns keys 4 k4 .. 4 k4 + 3 and dims 8 dc .. 8 dc + 7.
-  const int k4 = tid & 15, dc = tid >> 4;
-  float vf[4][8];
+  // Values: thread owns keys 4 k4 .. 4 k4 + 3 and dims 8 dc .. 8 dc + 7; per
+  // dim the largest magnitude over its keys, then over the 16 threads of the
+  // same dims (lanes that differ in their low four bits).
   {
-    float m = 0.0f;
+    const int k4 = tid & 15, dc = tid >> 4;
+    float vm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vm[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = tile * KT + 4 * k4 + i;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (key < S) val = v[((int64_t(seg_a) + key) * n_heads + h) * CHUNKS_PER_ROW + dc];
-      unpack8(val, vf[i]);
+      if (key < S) {
+        float f[8];
+        unpack8(v[((int64_t(seg_a) + key) * n_heads + h) * CHUNKS_PER_ROW + dc], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(vf[i][e]));
+        for (int j = 0; j < 8; ++j) vm[j] = fmaxf(vm[j], fabsf(f[j]));
+      }
     }
-    amax[4] = m;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) vm[j] = fmaxf(vm[j], __shfl_xor(vm[j], off));
+    }
+    if (k4 == 0) {
+      unsigned* am = v_amax + (int64_t(h) * gridDim.y + s) * D + 8 * dc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (vm[j] > 0.0f) atomicMax(am + j, __float_as_uint(vm[j]));
+    }
   }
 
-  // Block maxima: four key blocks and the value tile.
+  // Key block maxima over the workgroup.
 #pragma unroll
-  for (int j = 0; j < 5; ++j) {
+  for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], off));
   }
   if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < 5; ++j) s_red[wv][j] = amax[j];
+    for (int j = 0; j < 4; ++j) s_red[wv][j] = amax[j];
   }
   __syncthreads();
-  int ex[5];
+  int ex[4];
 #pragma unroll
-  for (int j = 0; j < 5; ++j)
+  for (int j = 0; j < 4; ++j)
     ex[j] = e4m3_scale_exponent(fmaxf(fmaxf(s_red[0][j], s_red[1][j]), fmaxf(s_red[2][j], s_red[3][j])));
   if (tid == 0) {
     unsigned w = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w |= unsigned(ex[j] + E8M0_ONE) << (8 * j);
     k_sc[int64_t(h) * tiles_per_head + prow / KT] = w;
-    v_sc[int64_t(h) * tiles_per_head + prow / KT] = unsigned(ex[4] + E8M0_ONE);
   }
 
   // Quantized keys: 8 bytes per chunk.
@@ -179,41 +218,74 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
     w[1] = pack_e4m3x4(kf[i][4] * down, kf[i][5] * down, kf[i][6] * down, kf[i][7] * down);
     k_ws[((int64_t(h) * rows_per_head + prow + r) * D) / 8 + cc] = w;
   }
+}
 
-  // Quantized values: for each of the thread's 8 dims, its 4 keys are 4
-  // consecutive bytes of that dim's row.
-  {
-    const float down = ldexpf(1.0f, -ex[4]);
-    const int pos0 = v8_key_byte(4 * k4);
-    unsigned* vt = v_ws + ((int64_t(h) * tiles_per_head + prow / KT) * D * KT) / 4;
+// ---------------------------------------------------------------------------
+// FP8 K/V prologue, pass 2: values.  grid = (64-key tiles, segments, heads),
+// 256 threads, after pass 1 has finished.
+// v_ws:   [H][rows/64][128][64] e4m3 values, transposed per tile, keys in the
+//         order v8_key_byte gives, each channel scaled by its segment's
+//         power of two (the exponent e4m3_scale_exponent gives for v_amax).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void v_quant_fp8_kernel(const u32x4* __restrict__ v, const int32_t* __restrict__ cu,
+                                                          int32_t n_heads, unsigned* __restrict__ v_ws,
+                                                          const unsigned* __restrict__ v_amax,
+                                                          int64_t rows_per_head, int32_t max_seqlen) {
+  const int tile = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int32_t seg_a = cu[s];
+  const int32_t S = min(cu[s + 1] - seg_a, max_seqlen);
+  if (tile * KT >= S) return;
+  const int tid = threadIdx.x;
+  const int64_t prow = packed_start(seg_a, s) + int64_t(tile) * KT;
+  const int64_t tiles_per_head = rows_per_head / KT;
+  // Thread owns keys 4 k4 .. 4 k4 + 3 and dims 8 dc .. 8 dc + 7; for each of
+  // its 8 dims, its 4 keys are 4 consecutive bytes of that dim's row.
+  const int k4 = tid & 15, dc = tid >> 4;
+  const unsigned* am = v_amax + (int64_t(h) * gridDim.y + s) * D + 8 * dc;
+  float down[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = 8 * dc + j;
-      vt[(d * KT + pos0) / 4] =
-          pack_e4m3x4(vf[0][j] * down, vf[1][j] * down, vf[2][j] * down, vf[3][j] * down);
-    }
+  for (int j = 0; j < 8; ++j) down[j] = ldexpf(1.0f, -e4m3_scale_exponent(__uint_as_float(am[j])));
+  float vf[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = tile * KT + 4 * k4 + i;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < S) val = v[((int64_t(seg_a) + key) * n_heads + h) * CHUNKS_PER_ROW + dc];
+    unpack8(val, vf[i]);
+  }
+  const int pos0 = v8_key_byte(4 * k4);
+  unsigned* vt = v_ws + ((int64_t(h) * tiles_per_head + prow / KT) * D * KT) / 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = 8 * dc + j;
+    vt[(d * KT + pos0) / 4] =
+        pack_e4m3x4(vf[0][j] * down[j], vf[1][j] * down[j], vf[2][j] * down[j], vf[3][j] * down[j]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // FP8 attention forward, software-pipelined inside each wave.
 //
-// Iteration t issues, in one branch-free block of 8 MFMA slots,
+// Iteration t issues, in one block of 8 MFMA slots,
 //     S(t+1) = K(t+1) Q^T      4 MFMAs (two subtiles x two 64-dim halves)
 //     O     += V(t-1) P(t-1)   4 MFMAs (one per 32-dim block of O^T)
 // and, after every slot, the exponentials of 4 of the 32 probabilities each
 // lane forms for tile t.  Consecutive score MFMAs share their query operand
 // and the four value MFMAs share the probabilities.
 //
-// Online softmax in base 2 with a lazily moved running maximum, as in the
-// bf16 kernel, here with the probabilities stored as p * 2^4: the running
-// value mm is the maximum minus 4, a tile's probabilities stay at most
-// 2^4 after a move and are rescaled once a lane's row sum for a tile
-// exceeds 256, so every stored probability is below 448.  The queries carry
-// the base-2 logit coefficient (scale * log2 e) into their quantization and
-// their power-of-two row scale rides on the matrix core's B scale, so a
-// score MFMA yields base-2 logits; its accumulator starts at -mm, so a
-// probability is one exp2 of the accumulator (no multiply-add per element).
+// Online softmax in base 2.  A score MFMA returns s = q8 . k8; the base-2
+// logit is z = cl * s with cl = scale * log2 e, and a probability is stored
+// as p' = exp2(cl * s - mm) = 256 p, where mm is the running reference minus
+// 8 (one multiply-add and one exp2 per element).  Dense instance: the
+// reference moves lazily.  A tile whose lane row sum of p' stays at most 448
+// needs nothing (every p' <= 448); otherwise the wave takes the tile's exact
+// maximum, and only where some p' could pass 448 (the tile's largest logit
+// more than P_ROOM_LOG2 above mm) moves the reference to that maximum,
+// rescales O and l and recomputes the tile.  Skip-Softmax instance: every
+// tile's maximum is taken for the skip rule anyway, so the reference is the
+// exact running maximum.  Either way O and l share one reference, so the
+// result is softmax over the kept keys with P rounded relative to a
+// reference within a factor 1.75 of the running maximum.
 //
 // LDS: rings of eight key slots and eight value slots of 8 KiB.  Iteration t
 // reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+5) and
@@ -225,7 +297,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
     RopeTable tab, const char* __restrict__ k_ws, const char* __restrict__ v_ws,
-    const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_sc, const int32_t* __restrict__ order,
+    const unsigned* __restrict__ k_sc, const unsigned* __restrict__ v_amax, const int32_t* __restrict__ order,
     int64_t rows_per_head, int32_t max_seqlen, float skip_log2, unsigned long long* __restrict__ skip_stats) {
   static_assert(F8_TILE_BYTES / 16 == F8_NW * 64, "one direct load per lane, tile and tensor");
 
@@ -251,7 +323,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   const char* kg = k_ws + (int64_t(h) * rows_per_head + prow) * D;
   const char* vg = v_ws + (int64_t(h) * rows_per_head + prow) * D;
   const unsigned* ksp = k_sc + int64_t(h) * tiles_per_head + prow / KT;
-  const unsigned* vsp = v_sc + int64_t(h) * tiles_per_head + prow / KT;
 
   // Direct loads: lane L of wave w fills LDS chunk p = 64 w + L of a slot
   // with the logical chunk the swizzle puts there.
@@ -287,11 +358,20 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   load_k(min(4, last_t), ic<4>());
   load_v(min(2, last_t), ic<2>());
 
+  // Value scales: lane L of value-dim block db carries the exponent scale of
+  // channel 32 db + L % 32 over this segment, for both 32-key halves.
+  unsigned vsc[4];
+  {
+    const unsigned* am = v_amax + (int64_t(h) * gridDim.z + s) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      vsc[db] = unsigned(e4m3_scale_exponent(__uint_as_float(am[32 * db + l32])) + E8M0_ONE);
+  }
+
   // Queries: B operand of S^T = K Q^T.  Lane holds query row l32 and, for
-  // half ks, dims 64 ks + 32 g .. + 31, rotated in fp32 and multiplied by
-  // the base-2 logit coefficient, then scaled by the row's power-of-two
-  // factor and rounded to e4m3; qsc is that factor's 8-bit exponent scale,
-  // which the score MFMAs apply.
+  // half ks, dims 64 ks + 32 g .. + 31, rotated in fp32, scaled by the row's
+  // power-of-two factor and rounded to e4m3; qsc is that factor's 8-bit
+  // exponent scale, which the score MFMAs apply.
   const int qrow = qt * F8_BQ + wave * 32 + l32;
   i32x8 qf[2];
   unsigned qsc;
@@ -318,12 +398,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
             rope_turn4(f[ks][j], rope_angles4(c * 4, s_omega, s_axis, pt, ph, pw));
           }
       }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[ks][j][e] *= scale_log2;
     } else {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -351,6 +425,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         qf[ks][w] = int(pack_e4m3x4(x[0] * down, x[1] * down, x[2] * down, x[3] * down));
       }
   }
+  const float cl = scale_log2;  // base-2 logit per unit of q8 . k8
 
   // Per-lane fragment offsets inside a slot (subtile, slot and 32-dim block
   // parts are immediates): K rows 32u + l32, chunks 4 ks + 2 g + hf; V^T rows
@@ -370,16 +445,14 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float mm = -INFINITY, l = 0.0f;
-  // Dense instance: score accumulators start at -moff (0 until mm is finite,
-  // then mm), so the exponentials need no subtraction.  The Skip-Softmax
-  // instance starts them at 0 and subtracts mm in the exponent: the start
-  // tuple's sixteen registers would push its loop into scratch reloads.
-  constexpr bool START_AT_M = !SKIP;
-  float moff = 0.0f;
-  float mt = -INFINITY;        // Skip-Softmax: largest base-2 logit of the tiles seen so far
+  float mm = -INFINITY, l = 0.0f;   // reference minus 8, and the row sum of p' = exp2(z - mm)
+  // Skip-Softmax: the row's largest base-2 logit over the tiles seen so far, the
+  // exponent offset of the current tile (mm, or +inf where the row leaves the
+  // tile out), this tile's rescale factor, and the row's counts.
+  float mt = -INFINITY, moff = 0.0f, resc = 1.0f;
   unsigned n_seen = 0, n_skipped = 0;
   bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
+  bool rescale = false;        // Skip-Softmax: some row of the wave moved its reference this tile
   f32x16 sc[2][2];          // S^T of one tile [buffer by tile parity][subtile]
   i32x8 pf[2];              // its e4m3 probabilities, by tile parity
 
@@ -405,16 +478,16 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     if (u == 0) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 0, int(ksw), 0, int(qsc));
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[ks], acc, 0, 0, 2, int(ksw), 0, int(qsc));
   };
-  auto mfma_pv = [&](f32x16 acc, i32x8 vf, const i32x8& p, unsigned vsc) __attribute__((always_inline)) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, p, acc, 0, 0, 0, int(vsc), 0, E8M0_ONE);
+  // Value products: per-lane channel scales on V^T, p' unscaled.
+  auto mfma_pv = [&](f32x16 acc, i32x8 vf, const i32x8& p, int db) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, p, acc, 0, 0, 0, int(vsc[db]), 0, E8M0_ONE);
   };
   // Per-lane exponent scales of K tile t (subtile 0 in byte 0, subtile 1 in
-  // byte 2, both in k0; k1 carries the same word), and V tile t's.
+  // byte 2, both in k0; k1 carries the same word).
   auto kscales = [&](int t, unsigned& k0, unsigned& k1) __attribute__((always_inline)) {
     k0 = ksp[t] >> ksh0;
     k1 = k0;
   };
-  auto vscale = [&](int t) __attribute__((always_inline)) { return vsp[t]; };
 
   // S^T(t) into buffer B, alone (pipeline fill).
   auto qk_alone = [&](auto B, auto SLOT, unsigned k0, unsigned k1) __attribute__((always_inline)) {
@@ -423,17 +496,17 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     for (int u = 0; u < 2; ++u) {
       f32x16 acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = START_AT_M ? -moff : 0.0f;
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) acc = mfma_qk(acc, kfrag(SLOT, u, ks), ks, u, u ? k1 : k0);
       sc[b][u] = acc;
     }
   };
   // O^T += V^T(t) P^T(t) from buffer B, alone (pipeline drain).
-  auto pv_alone = [&](auto B, auto SLOT, unsigned vsc) __attribute__((always_inline)) {
+  auto pv_alone = [&](auto B, auto SLOT) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma_pv(o[db], vfrag(SLOT, db), pf[b], vsc);
+    for (int db = 0; db < 4; ++db) o[db] = mfma_pv(o[db], vfrag(SLOT, db), pf[b], db);
   };
   // Keys of tile t at or past the segment end get score -inf.  Key (u, r) of
   // this lane is t*64 + 32u + 8(r/4) + 4g + r%4: compare the constant part
@@ -449,14 +522,24 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         sc[b][u][r] = 32 * u + 8 * (r >> 2) + (r & 3) < lim ? x : -INFINITY;
       }
   };
+  // The lane's largest raw score of the tile in buffer B, with its partner's.
+  auto tile_max = [&](auto B) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    float mx = sc[b][0][0];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
+    return pair_max(mx);
+  };
   // Unit j (0..7) of tile t's probabilities (scores in buffer B): word j of
   // the lane's 32 bytes, i.e. subtile j / 4, registers 4 (j % 4) .. + 3.
   auto exp_unit = [&](auto B, int j, float (&p)[4]) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
+    const float off = SKIP ? moff : mm;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x = sc[b][j >> 2][4 * (j & 3) + i];
-      p[i] = __builtin_amdgcn_exp2f(START_AT_M ? x : x - mm);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cl, -off));
       pin(p[i]);
     }
   };
@@ -470,48 +553,49 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     pw[j] = int(w);
     rs = r;
   };
-  // After the exponentials of tile t (buffer B): the rare path that moves the
-  // running maximum (rescaling O and l, recomputing the tile's probabilities
-  // and, when the scores of tile t+1 are already under way (PENDING), moving
-  // them to the new start), then the row sum.  The first tile always takes
-  // it: mm is still -inf there.
-  auto settle = [&](auto B, auto PENDING, i32x8& pw, float rs) __attribute__((always_inline)) {
+  // After the exponentials of tile t (buffer B, products of tile t-1 issued).
+  // Dense instance: the rare path that moves the reference, then the row sum.
+  // The first tile always takes it (mm is still -inf there).  Skip-Softmax
+  // instance: the reference was set before the exponentials; here O and l are
+  // rescaled to it (after the products of tile t-1, which used the old one).
+  auto settle = [&](auto B, i32x8& pw, float rs) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
-    const bool over = !(rs <= LAZY_SUM) || mm == -INFINITY;  // also true for inf and NaN
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {
-      float mx = sc[b][0][0];
+    if constexpr (SKIP) {
+      if (rescale) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
-      const float tmax = pair_max(mx) + moff;
-      const float m_new = fmaxf(mm, tmax - P_SHIFT);
-      const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf
-      const float shift = moff - m_new;
-      mm = m_new;
-      if constexpr (START_AT_M) moff = m_new;
-      l *= a;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= a;
-      rs = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[b][j >> 2][4 * (j & 3) + i] + shift);
-        pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
-        rs += (p[0] + p[1]) + (p[2] + p[3]);
+          for (int r = 0; r < 16; ++r) o[db][r] *= resc;
       }
-      if constexpr (START_AT_M && decltype(PENDING)::value != 0) {
+      l = l * resc + rs;
+    } else {
+      const bool over = !(rs <= E4M3_TOP);  // also true for inf and NaN (the first tile)
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        const float tmax = tile_max(ic<b>()) * cl;
+        const bool move = !(tmax - mm <= P_ROOM_LOG2);  // some p' could pass 448 (or mm = -inf)
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float m_new = move ? fmaxf(mm, tmax - P_SHIFT) : mm;
+          const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf, 1 where unmoved
+          mm = m_new;
+          l *= a;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sc[1 - b][u][r] += shift;
+            for (int r = 0; r < 16; ++r) o[db][r] *= a;
+          rs = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cl, -mm));
+            pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
+            rs += (p[0] + p[1]) + (p[2] + p[3]);
+          }
+        }
       }
+      l += rs;
     }
-    l += rs;
   };
 
   // Iteration t, B = t mod 2 (S(t) in sc[B], P(t-1) in pf[1 - B]), reading
@@ -528,7 +612,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // wave-uniform branch, the value MFMAs under a third (a left-out tile then
   // skips three branches, where interleaving needed twelve).
   auto region = [&](auto B, auto QK, auto PV, bool do_exp, bool pv_live, auto kslot, auto vslot, unsigned k0,
-                    unsigned k1, unsigned vsc) __attribute__((always_inline)) {
+                    unsigned k1) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     constexpr bool do_qk = decltype(QK)::value != 0;
     constexpr bool do_pv = decltype(PV)::value != 0;
@@ -577,7 +661,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         if (pv_live) {
 #pragma unroll
           for (int j = 4; j < 8; ++j) {
-            o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
+            o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], j - 4);
             if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
           }
         }
@@ -598,12 +682,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           const int u = j & 1, ks = j >> 1;
           f32x16 acc;
           if (ks == 0) {
-            if constexpr (START_AT_M) {
-              acc = splat16(-moff);  // the first half starts the chain at -moff
-            } else {
   #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            }
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
           } else {
             acc = sc[1 - b][u];
           }
@@ -624,7 +704,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   #pragma unroll
       for (int j = 4; j < 8; ++j) {
         if (do_pv) {
-          if (pv_live) o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], vsc);
+          if (pv_live) o[j - 4] = mfma_pv(o[j - 4], fr[j & 1], pf[1 - b], j - 4);
           if (j < 6) fr[j & 1] = vfrag(vslot, j - 2);
         }
         if (do_exp) {
@@ -636,39 +716,43 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       }
     }
     if (do_exp) {
-      settle(ic<b>(), QK, pw, rs);
+      settle(ic<b>(), pw, rs);
       pf[b] = pw;
     }
   };
 
-  // Skip-Softmax decision for tile t (scores in buffer B): the wave leaves the
-  // tile out when each of its rows has a tile maximum below its running
-  // maximum of earlier tiles times the threshold (rows past the segment end
-  // do not vote).  Updates the running maximum; returns the uniform decision.
+  // Skip-Softmax decision for tile t (scores in buffer B), per row: the row
+  // leaves the tile out when its largest logit in the tile is below its
+  // largest logit over the earlier tiles plus log2 of the threshold; rows past
+  // the segment end leave every tile out.  Sets the row's exponent offset and
+  // its reference (the running maximum, which only a kept tile can raise) and
+  // the rescale factor settle applies; counts the row's decisions.  Returns
+  // whether the whole wave leaves the tile out.
   auto decide = [&](auto B) __attribute__((always_inline)) {
-    constexpr int b = decltype(B)::value;
-    float mx = sc[b][0][0];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
-    const float tm = pair_max(mx) + moff;
-    const bool lets_go = qrow >= S || tm < mt + skip_log2;
+    const float tm = tile_max(B) * cl;
+    const bool valid = qrow < S;
+    const bool lets_go = !valid || tm < mt + skip_log2;
     mt = fmaxf(mt, tm);
+    const float m_new = fmaxf(mm, mt - P_SHIFT);
+    resc = __builtin_amdgcn_exp2f(mm - m_new);  // 1 where unmoved, 0 from -inf
+    rescale = __builtin_amdgcn_ballot_w64(m_new != mm) != 0;
+    mm = m_new;
+    moff = lets_go ? INFINITY : mm;
+    n_seen += valid ? 1u : 0u;
+    n_skipped += (valid && lets_go) ? 1u : 0u;
     return __builtin_amdgcn_ballot_w64(!lets_go) == 0;
   };
-  // Iteration t under Skip-Softmax: the exponentials of tile t only if the
-  // wave keeps it, the products of tile t-1 only if it kept that one.
-  auto region_skip = [&](auto B, auto QK, auto kslot, auto vslot, unsigned k0, unsigned k1, unsigned vsc, bool skip)
+  // Iteration t under Skip-Softmax: the exponentials of tile t only if some
+  // row of the wave keeps it, the products of tile t-1 only if some row kept
+  // that one.
+  auto region_skip = [&](auto B, auto QK, auto kslot, auto vslot, unsigned k0, unsigned k1, bool skip)
       __attribute__((always_inline)) {
-    region(B, QK, ic<1>(), !skip, prev_kept, kslot, vslot, k0, k1, vsc);
+    region(B, QK, ic<1>(), !skip, prev_kept, kslot, vslot, k0, k1);
     prev_kept = !skip;
-    ++n_seen;
-    n_skipped += skip ? 1u : 0u;
   };
 
-  // Scales for the products iteration t issues: K(t+1) and V(t-1).
-  unsigned kq0, kq1, vq;
+  // Scales for the products iteration t issues: K(t+1).
+  unsigned kq0, kq1;
   // Steady iteration t (1 <= t <= last_t - 1), T8 = t mod 8.  Loads K(t+5) and
   // V(t+3).  Iterations pair up into epochs (t odd, t+1) that end with one
   // barrier: within an epoch no slot that is read is also written, and
@@ -679,13 +763,12 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   auto step = [&](auto T8, int t) __attribute__((always_inline)) {
     constexpr int t8 = decltype(T8)::value;
     if constexpr (SKIP)
-      region_skip(ic<t8 & 1>(), ic<1>(), ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq, decide(ic<t8 & 1>()));
+      region_skip(ic<t8 & 1>(), ic<1>(), ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, decide(ic<t8 & 1>()));
     else
-      region(ic<t8 & 1>(), ic<1>(), ic<1>(), true, true, ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1, vq);
+      region(ic<t8 & 1>(), ic<1>(), ic<1>(), true, true, ic<(t8 + 1) & 7>(), ic<(t8 + 7) & 7>(), kq0, kq1);
     load_k(min(t + 5, last_t), ic<(t8 + 5) & 7>());
     load_v(min(t + 3, last_t), ic<(t8 + 3) & 7>());
     kscales(min(t + 2, last_t), kq0, kq1);
-    vq = vscale(t);
     if ((t8 & 1) == 0) ring_barrier<4>();  // end of an epoch: its loads may stay in flight
   };
   // Last iteration t = last_t >= 1, B = t mod 2: exponentials of tile t and
@@ -695,13 +778,12 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     constexpr int b = decltype(B)::value;
     mask_tail(ic<b>(), last_t);
     if constexpr (SKIP)
-      region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, vq, decide(ic<b>()));
+      region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, decide(ic<b>()));
     else
-      region(ic<b>(), ic<0>(), ic<1>(), true, true, 0, (last_t - 1) & 7, kq0, kq1, vq);
-    const unsigned vl = vscale(last_t);
+      region(ic<b>(), ic<0>(), ic<1>(), true, true, 0, (last_t - 1) & 7, kq0, kq1);
     ring_barrier<0>();  // V(t) has landed
     __builtin_amdgcn_sched_barrier(0);
-    if (prev_kept) pv_alone(ic<b>(), last_t & 7, vl);
+    if (prev_kept) pv_alone(ic<b>(), last_t & 7);
   };
   {
     unsigned k0, k1;
@@ -710,24 +792,19 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   }
   if (n_kt == 1) {
     mask_tail(ic<0>(), 0);
-    if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept; this seeds the running maximum
-    region(ic<0>(), ic<0>(), ic<0>(), true, true, ic<1>(), ic<7>(), 0u, 0u, 0u);
-    const unsigned vl = vscale(0);
+    if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
+    region(ic<0>(), ic<0>(), ic<0>(), true, true, ic<1>(), ic<7>(), 0u, 0u);
     ring_barrier<0>();
-    pv_alone(ic<0>(), ic<0>(), vl);
+    pv_alone(ic<0>(), ic<0>());
   } else {
     ring_barrier<6>();  // every wave is done with K(0) before its slot is refilled
     kscales(1, kq0, kq1);
     // t = 0: no products of an earlier tile yet; an epoch of its own.
-    if constexpr (SKIP) {
-      (void)decide(ic<0>());  // the first tile is always kept; this seeds the running maximum
-      ++n_seen;
-    }
-    region(ic<0>(), ic<1>(), ic<0>(), true, true, ic<1>(), ic<7>(), kq0, kq1, 0u);
+    if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
+    region(ic<0>(), ic<1>(), ic<0>(), true, true, ic<1>(), ic<7>(), kq0, kq1);
     load_k(min(5, last_t), ic<5>());
     load_v(min(3, last_t), ic<3>());
     kscales(min(2, last_t), kq0, kq1);
-    vq = vscale(0);
     ring_barrier<4>();
     int t = 1;
     for (; t + 7 <= last_t - 1; t += 8) {
@@ -757,7 +834,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
       last(ic<0>());
   }
 
-  // Epilogue: O = O / l, lse = (mm + log2 l) * ln 2 (the 2^4 of the stored
+  // Epilogue: O = O / l, lse = (mm + log2 l) * ln 2 (the 2^8 of the stored
   // probabilities cancels: mm and l carry it with opposite signs).
   const float lt = pair_sum(l);
   const float inv = 1.0f / lt;
@@ -776,10 +853,19 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     if (g == 0) lse[int64_t(h) * n_tokens + tok] = (mm + log2f(lt)) * 0.69314718055994531f;
   }
   if constexpr (SKIP) {
-    // tiles seen and left out by this wave (if any of its rows exists), for callers that ask
-    if (skip_stats != nullptr && lane == 0 && qt * F8_BQ + wave * 32 < S) {
-      atomicAdd(&skip_stats[0], (unsigned long long)(n_kt == 1 ? 1u : n_seen));
-      atomicAdd(&skip_stats[1], (unsigned long long)n_skipped);
+    // (row, tile) pairs seen and left out by this wave's rows, for callers that ask; lane L and
+    // L + 32 hold the same row, so only the lower half counts
+    if (skip_stats != nullptr) {
+      unsigned long long seen = g == 0 ? n_seen : 0u, left = g == 0 ? n_skipped : 0u;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        seen += __shfl_xor(seen, off);
+        left += __shfl_xor(left, off);
+      }
+      if (lane == 0 && seen != 0) {
+        atomicAdd(&skip_stats[0], seen);
+        atomicAdd(&skip_stats[1], left);
+      }
     }
   }
 }
@@ -787,20 +873,28 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 
 int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, const float* pos, int32_t n_heads,
                            int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws, void* v_ws,
-                           unsigned* k_sc, unsigned* v_sc, int32_t* order, int64_t rows_per_head, void* stream) {
+                           unsigned* k_sc, unsigned* v_amax, int32_t* order, int64_t rows_per_head, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + KT - 1) / KT);
   if (tiles == 0) return 0;
-  hipLaunchKernelGGL(kv_prologue_fp8_kernel, dim3(tiles, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
-                     cu, pos, n_heads, table, static_cast<u32x2*>(k_ws), static_cast<unsigned*>(v_ws), k_sc, v_sc,
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The channel maxima are raised from 0 by atomic max: clear them first (a fill kernel, so that the
+  // sequence may be captured in a graph).
+  const int64_t n_amax = int64_t(n_heads) * n_seqs * D;
+  const unsigned clear_blocks = unsigned(std::min<int64_t>((n_amax + 255) / 256, 4096));
+  hipLaunchKernelGGL(fp8_clear_kernel, dim3(clear_blocks), dim3(256), 0, st, v_amax, n_amax);
+  const dim3 grid(tiles, unsigned(n_seqs), unsigned(n_heads));
+  hipLaunchKernelGGL(kv_prologue_fp8_kernel, grid, dim3(256), 0, st, static_cast<const u32x4*>(k),
+                     static_cast<const u32x4*>(v), cu, pos, n_heads, table, static_cast<u32x2*>(k_ws), k_sc, v_amax,
                      order, rows_per_head, max_seqlen);
+  hipLaunchKernelGGL(v_quant_fp8_kernel, grid, dim3(256), 0, st, static_cast<const u32x4*>(v), cu, n_heads,
+                     static_cast<unsigned*>(v_ws), static_cast<const unsigned*>(v_amax), rows_per_head, max_seqlen);
   return int(hipGetLastError());
 }
 
 int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
                          int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
                          float skip_threshold, const RopeTable& table, const void* k_ws, const void* v_ws,
-                         const unsigned* k_sc, const unsigned* v_sc, const int32_t* order, int64_t rows_per_head,
+                         const unsigned* k_sc, const unsigned* v_amax, const int32_t* order, int64_t rows_per_head,
                          unsigned long long* skip_stats, void* stream) {
   const unsigned tiles = unsigned((int64_t(max_seqlen) + F8_BQ - 1) / F8_BQ);
   if (tiles == 0) return 0;
@@ -826,12 +920,12 @@ int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, voi
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, grid, dim3(F8_NW * 64), F8_SMEM, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(q), cu, pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens),
                        n_heads, scale_log2, table, static_cast<const char*>(k_ws), static_cast<const char*>(v_ws),
-                       k_sc, v_sc, order, rows_per_head, max_seqlen, skip_log2, skip_stats);
+                       k_sc, v_amax, order, rows_per_head, max_seqlen, skip_log2, skip_stats);
   else
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, grid, dim3(F8_NW * 64), F8_SMEM,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu, pos,
                        static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
-                       static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_sc, order,
+                       static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_amax, order,
                        rows_per_head, max_seqlen, 0.0f, nullptr);
   return int(hipGetLastError());
 }

@@ -64,21 +64,22 @@ inline WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_heads, int32
 //   keys    e4m3 [H][rows][128]            rotated keys
 //   values  e4m3 [H][rows/64][128][64]     transposed 64-key tiles
 //   kscale  u32  [H][rows/64]              per tile: 4 exponent scales of 16 keys
-//   vscale  u32  [H][rows/64]              per tile: the exponent scale of its values
+//   vamax   u32  [H][n_seqs][128]          per value channel, the largest magnitude over the segment
 //   order   i32  [n_seqs]                  segments by length, longest first
 struct WorkspaceLayoutFp8 {
-  size_t keys_offset, values_offset, kscale_offset, vscale_offset, order_offset, total;
+  size_t keys_offset, values_offset, kscale_offset, vamax_offset, order_offset, total;
 };
 inline WorkspaceLayoutFp8 workspace_layout_fp8(int64_t n_tokens, int32_t n_heads, int32_t n_seqs) {
   const size_t rows = size_t(packed_rows(n_tokens, n_seqs));
   const size_t plane = size_t(n_heads) * rows * kHeadDim;
-  const size_t scales = (size_t(n_heads) * (rows / kKeyTile) * 4 + 255) / 256 * 256;
+  const size_t kscales = align256(size_t(n_heads) * (rows / kKeyTile) * 4);
+  const size_t vamax = align256(size_t(n_heads) * size_t(n_seqs) * kHeadDim * 4);
   WorkspaceLayoutFp8 w;
   w.keys_offset = 0;
   w.values_offset = plane;
   w.kscale_offset = 2 * plane;
-  w.vscale_offset = 2 * plane + scales;
-  w.order_offset = 2 * plane + 2 * scales;
+  w.vamax_offset = 2 * plane + kscales;
+  w.order_offset = 2 * plane + kscales + vamax;
   w.total = w.order_offset + size_t(n_seqs) * 4;
   return w;
 }
@@ -96,11 +97,11 @@ int launch_attention(const void* q, const int32_t* cu, const float* pos, void* o
                      int64_t rows_per_head, void* stream);
 int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, const float* pos, int32_t n_heads,
                            int32_t n_seqs, int32_t max_seqlen, const RopeTable& table, void* k_ws, void* v_ws,
-                           unsigned* k_sc, unsigned* v_sc, int32_t* order, int64_t rows_per_head, void* stream);
+                           unsigned* k_sc, unsigned* v_amax, int32_t* order, int64_t rows_per_head, void* stream);
 int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, void* out, float* lse,
                          int64_t n_tokens, int32_t n_heads, int32_t n_seqs, int32_t max_seqlen, float scale,
                          float skip_threshold, const RopeTable& table, const void* k_ws, const void* v_ws,
-                         const unsigned* k_sc, const unsigned* v_sc, const int32_t* order, int64_t rows_per_head,
+                         const unsigned* k_sc, const unsigned* v_amax, const int32_t* order, int64_t rows_per_head,
                          unsigned long long* skip_stats, void* stream);
 const char* hip_error_string(int err);
 

@@ -175,9 +175,11 @@ def ragged_segments():
 #     independent roundings whose standard deviation the oracle reports
 #     ("sigma").  Bound: 6 sigma, plus the bf16 rounding of out (2^-8 of
 #     |out|), plus 1e-4 for fp32 accumulation order.
-#   * fp32 evaluation of the scores: 128 exact fp8 products summed in fp32, an
-#     error of a few 2^-24 of the sum of their magnitudes ("zabs" per row), so
-#     lse within 2^-16 zabs + 1e-5.
+#   * evaluation of the scores: the scaled fp8 products are summed by the matrix
+#     core, whose accumulation is not exact fp32: on logits of several hundred
+#     (q x 64) lse moved by up to 2^-15.8 of the row's largest sum of absolute
+#     products ("zabs" per row).  Bound: lse within 2^-14 zabs + 1e-5, the same
+#     evaluation error the oracle allows each logit for Skip-Softmax decisions.
 #   * rounding decisions: the kernel rotates in fp32 arithmetic of its own and
 #     the oracle rounds the float64 rotation to fp32; where an e4m3 rounding
 #     midpoint (or a block-scale boundary) lies within their error window, both
@@ -204,7 +206,7 @@ def ragged_segments():
 # checked against the quantized oracle only; their distance from exact softmax
 # grows with the logits and is reported.
 FP8_SIGMAS = 6.0
-FP8_LSE_REL = 2.0 ** -16
+FP8_LSE_REL = 2.0 ** -14
 FP8_LSE_ABS = 1e-5
 FP8_EXACT_OUT_MAX = 0.5
 FP8_EXACT_OUT_MEAN = 2e-2

@@ -216,13 +216,16 @@ def test_workspace_size_formula(L):
 
 
 def test_fp8_workspace_size_formula(L):
-    # per head: 64 * (ceil(N / 64) + n_seqs) rows of 128 bytes for keys and for values, then two
-    # arrays of one 32-bit word per 64-row tile (key scales, value scales), each padded to 256 bytes,
-    # then one int32 per segment (the segments' order by length)
+    # per head: 64 * (ceil(N / 64) + n_seqs) rows of 128 bytes for keys and for values, then one
+    # 32-bit word per 64-row tile (key scales) and one per (head, segment, value channel) (the
+    # channels' largest magnitudes), each padded to 256 bytes, then one int32 per segment (the
+    # segments' order by length)
     for N, Hh, ns in [(1, 1, 1), (64, 2, 1), (65, 3, 4), (130048, 5, 1), (45760, 16, 4), (2542, 56, 8)]:
         rows = 64 * ((N + 63) // 64 + ns)
-        scales = (Hh * (rows // 64) * 4 + 255) // 256 * 256
-        assert L.h3attn_varlen_fwd_fp8_workspace_size(N, Hh, 128, ns) == 2 * Hh * rows * 128 + 2 * scales + 4 * ns
+        kscales = (Hh * (rows // 64) * 4 + 255) // 256 * 256
+        vamax = (Hh * ns * 128 * 4 + 255) // 256 * 256
+        assert L.h3attn_varlen_fwd_fp8_workspace_size(N, Hh, 128, ns) == \
+            2 * Hh * rows * 128 + kscales + vamax + 4 * ns
     assert L.h3attn_varlen_fwd_fp8_workspace_size(10, 1, 64, 1) == 0
 
 
