@@ -178,6 +178,26 @@ h3attn_status h3attn_varlen_attention(const void* q, const int32_t* cu_seqlens, 
                                       void* stream);
 
 /* ---------------------------------------------------------------------
+ * h3attn_varlen_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and checks are
+ * h3attn_varlen_fwd's minus the workspace: the library uses a 128 MiB array
+ * of its own on each GPU instead, held from the library's load until the
+ * process ends, and allocates nothing.  Fails with UNSUPPORTED, before any
+ * launch, when h3attn_varlen_fwd_workspace_size(n_tokens, n_heads, head_dim,
+ * n_seqs) exceeds 134,217,728 bytes (about 250,000 (token, head) pairs: the
+ * 480p-shaped workload fits, the 1344x768-shaped one does not).  All calls on
+ * one GPU share its array and find it as the last call left it; every call
+ * rewrites all of it that it reads, so calls in order on one stream are safe,
+ * while calls that overlap in time on one GPU (other streams or threads) race
+ * and give wrong results.
+ * ------------------------------------------------------------------- */
+h3attn_status h3attn_varlen_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                        const float* pos_thw, void* out, float* lse, int64_t n_tokens,
+                                        int32_t n_heads, int32_t head_dim, int32_t n_seqs, int32_t max_seqlen,
+                                        float softmax_scale, const h3attn_rope_cfg* rope, void* stream);
+
+/* ---------------------------------------------------------------------
  * Lossy FP8 mode of the same attention ("SAGE" quantization).
  *
  * Defined by the vLLM-Omni "MiniMax-H3" recipe, section "Attention

@@ -262,6 +262,33 @@ h3attn_status h3attn_varlen_fwd(const void* q, const void* k, const void* v, con
   }
 }
 
+h3attn_status h3attn_varlen_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                        const float* pos_thw, void* out, float* lse, int64_t n_tokens,
+                                        int32_t n_heads, int32_t head_dim, int32_t n_seqs, int32_t max_seqlen,
+                                        float softmax_scale, const h3attn_rope_cfg* rope, void* stream) {
+  try {
+    clear_error();
+    h3attn_status st = check_varlen(n_tokens, n_heads, head_dim, n_seqs, max_seqlen);
+    if (st != H3ATTN_OK) return st;
+    RopeTable table;
+    st = make_rope_table(rope, head_dim, &table);
+    if (st != H3ATTN_OK) return st;
+    if (!std::isfinite(softmax_scale)) return fail(H3ATTN_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (n_tokens == 0) return H3ATTN_OK;
+    if (workspace_bytes_for(n_tokens, n_heads, n_seqs) > kNoAllocScratchBytes)
+      return fail(H3ATTN_ERR_UNSUPPORTED,
+                  "the call needs more workspace than the library's 128 MiB array "
+                  "(h3attn_varlen_fwd_workspace_size > 134217728): use h3attn_varlen_fwd");
+    void* ws = nullptr;
+    const int e = noalloc_workspace(&ws);
+    if (e != 0) return hip_status(e);
+    return h3attn_varlen_fwd(q, k, v, cu_seqlens, pos_thw, out, lse, n_tokens, n_heads, head_dim, n_seqs, max_seqlen,
+                             softmax_scale, rope, ws, kNoAllocScratchBytes, stream);
+  } catch (...) {
+    return fail(H3ATTN_ERR_INVALID_ARG, "unexpected host exception in h3attn_varlen_fwd_noalloc");
+  }
+}
+
 size_t h3attn_varlen_fwd_fp8_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs) {
   if (n_tokens < 0 || n_heads < 1 || head_dim != kHeadDim || n_seqs < 1) return 0;
   return workspace_layout_fp8(n_tokens, n_heads, n_seqs).total;

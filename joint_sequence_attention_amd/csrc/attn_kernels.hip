@@ -44,6 +44,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "device_common.h"
 
@@ -662,9 +663,34 @@ __global__ __launch_bounds__(P_NW * 64, 1) void attn_fwd_kernel(
     if (g == 0) lse[int64_t(h) * n_tokens + tok] = (m + log2f(lt)) * 0.69314718055994531f;
   }
 }
+// Workspace of the no-allocation entry point: one array per GPU, held from the
+// code object's load until the process ends.  Host code never uses this name
+// as an address: it takes the device address from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
 }  // namespace
 
 const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+int noalloc_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kMaxDevices) return int(hipErrorInvalidDevice);
+  // The address is looked up once per device, with that device current, and kept.
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return int(e);
+    if (p == nullptr) return int(hipErrorInvalidSymbol);
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
+}
 
 int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,
                       const RopeTable& table, void* stream) {

@@ -84,6 +84,13 @@ inline WorkspaceLayoutFp8 workspace_layout_fp8(int64_t n_tokens, int32_t n_heads
   return w;
 }
 
+// Workspace of h3attn_varlen_fwd_noalloc: a file-scope device array of this
+// size on each GPU (attn_kernels.hip).  noalloc_workspace() returns its device
+// address on the current device (looked up once per device) or a HIP error.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+int noalloc_workspace(void** ptr);
+
 // Kernel launchers (attn_kernels.hip, attn_fp8.hip).  They only enqueue; the caller has
 // validated every argument.  Return hipSuccess or the launch error.
 int launch_rope_apply(const void* x, void* y, const float* pos, int64_t n_tokens, int32_t n_heads,

@@ -97,6 +97,9 @@ def lib():
     L.h3attn_varlen_attention_fp8.restype = ctypes.c_int
     L.h3attn_varlen_attention_fp8.argtypes = [vp, vp, vp, vp, vp, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.c_float,
                                               ctypes.c_float, rp, vp, c_sz, vp, vp]
+    L.h3attn_varlen_fwd_noalloc.restype = ctypes.c_int
+    L.h3attn_varlen_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, c_i64, c_i32, c_i32, c_i32, c_i32,
+                                            ctypes.c_float, rp, vp]
     L.h3attn_skip_gate.restype = ctypes.c_int
     L.h3attn_skip_gate.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float)]
     _lib = L
@@ -111,6 +114,7 @@ EXPORTED = (
     "h3attn_varlen_fwd",
     "h3attn_varlen_kv_prologue",
     "h3attn_varlen_attention",
+    "h3attn_varlen_fwd_noalloc",
     "h3attn_varlen_fwd_fp8_workspace_size",
     "h3attn_varlen_fwd_fp8",
     "h3attn_varlen_kv_prologue_fp8",
@@ -279,6 +283,29 @@ def h3attn_varlen_fwd(q, k, v, cu_seqlens, pos_thw, max_seqlen, out=None, lse=No
                                    int(max_seqlen), float(softmax_scale), ctypes.byref(cfg), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
            "h3attn_varlen_fwd")
+    return out, lse
+
+
+def h3attn_varlen_fwd_noalloc(q, k, v, cu_seqlens, pos_thw, max_seqlen, out=None, lse=None, softmax_scale=0.0,
+                              theta=DEFAULT_THETA, dims=DEFAULT_DIMS, stream=None):
+    """h3attn_varlen_fwd on the library's own scratch array (no workspace argument, no allocation by the
+    library); out and lse are allocated here when not given.  Returns (out, lse)."""
+    torch = _torch()
+    N, H, Dh, n_seqs = _varlen_common(q, cu_seqlens, pos_thw, max_seqlen)
+    _need(k, torch.bfloat16, q.shape, "k")
+    _need(v, torch.bfloat16, q.shape, "v")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    _need(out, torch.bfloat16, q.shape, "out")
+    _need(lse, torch.float32, (H, N), "lse")
+    cfg = rope_cfg(theta, dims)
+    _check(lib().h3attn_varlen_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                           pos_thw.data_ptr(), out.data_ptr(), lse.data_ptr(), N, H, Dh, n_seqs,
+                                           int(max_seqlen), float(softmax_scale), ctypes.byref(cfg),
+                                           _stream_ptr(stream)),
+           "h3attn_varlen_fwd_noalloc")
     return out, lse
 
 

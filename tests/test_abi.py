@@ -268,3 +268,23 @@ def test_max_seqlen_limit(L):
                                            wsb8, None) == H.H3ATTN_ERR_UNSUPPORTED
     assert L.h3attn_varlen_attention_fp8(FAKE, FAKE * 4, FAKE * 5, big, 2 * big, N, 1, 128, 1, N, 0.0, 0.0, _cfg(),
                                          4 * big, wsb8, None, None) == H.H3ATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_checks_before_any_launch(L):
+    # the no-allocation entry point refuses a call beyond its 128 MiB array, and bad arguments,
+    # before it touches the GPU; N = 0 is a no-op
+    cfg = _cfg()
+    big = 1 << 44
+    st = L.h3attn_varlen_fwd_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, big, 2 * big, 130048, 5, 128, 1,
+                                     130048, 0.0, cfg, None)
+    assert st == H.H3ATTN_ERR_UNSUPPORTED and "128 MiB" in H.h3attn_last_error()
+    assert L.h3attn_varlen_fwd_workspace_size(130048, 5, 128, 1) > 128 << 20
+    assert L.h3attn_varlen_fwd_workspace_size(7936, 24, 128, 1) <= 128 << 20
+    assert L.h3attn_varlen_fwd_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, big, 2 * big, 64, 2, 64, 1, 64,
+                                       0.0, cfg, None) == H.H3ATTN_ERR_UNSUPPORTED
+    assert L.h3attn_varlen_fwd_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, big, 2 * big, 64, 2, 128, 1, 65,
+                                       0.0, cfg, None) == H.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_varlen_fwd_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, big, 2 * big, 64, 2, 128, 1, 64,
+                                       float("nan"), cfg, None) == H.H3ATTN_ERR_INVALID_ARG
+    assert L.h3attn_varlen_fwd_noalloc(None, None, None, None, None, None, None, 0, 2, 128, 1, 0, 0.0, cfg,
+                                       None) == H.H3ATTN_OK
