@@ -22,11 +22,13 @@
 //
 // Kernels:
 //   fp8_clear_kernel        zeroes the per-channel value maxima.
+//   v_amax_fp8_kernel       takes each value channel's largest magnitude over
+//                           its segment: a reduction over 1024 keys per
+//                           workgroup, then one atomic max per channel.
 //   kv_prologue_fp8_kernel  rotates K, quantizes it in 16-key blocks and packs
-//                           it into 64-key tiles; takes each value channel's
-//                           largest magnitude over its segment (atomic max).
-//   v_quant_fp8_kernel      quantizes V with those channel scales and packs it,
-//                           transposed, into 64-key tiles.  Both HBM-bound.
+//                           it into 64-key tiles.
+//   v_quant_fp8_kernel      quantizes V with the channel scales and packs it,
+//                           transposed, into 64-key tiles.  All HBM-bound.
 //   attn_fwd_fp8_kernel     one workgroup per (256-query tile, head, segment
 //                           rank), longest segments first; eight waves, 32
 //                           queries per wave; 64-key tiles through LDS rings;
@@ -101,22 +103,77 @@ __global__ __launch_bounds__(256) void fp8_clear_kernel(unsigned* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// FP8 K/V prologue, pass 1.  grid = (64-key tiles of the longest segment,
+// Value channel maxima.  grid = (VA_KEYS-key chunks of the longest segment,
+// segments, heads), 256 threads.
+// v_amax: [H][n_seqs][128] per value channel, the largest magnitude over the
+//         segment (float bit patterns, which order like the values since they
+//         are >= 0); raised here with atomic max from 0.  One atomic per
+//         channel and chunk: the atomics of a segment all land on four cache
+//         lines per head, so their number, not the bytes read, sets the time
+//         when a chunk is small.
+// ---------------------------------------------------------------------------
+constexpr int VA_KEYS = 1024;
+__global__ __launch_bounds__(256) void v_amax_fp8_kernel(const u32x4* __restrict__ v, const int32_t* __restrict__ cu,
+                                                         int32_t n_heads, unsigned* __restrict__ v_amax,
+                                                         int32_t max_seqlen) {
+  __shared__ float s_red[4][D];
+  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int32_t seg_a = cu[s];
+  const int32_t S = min(cu[s + 1] - seg_a, max_seqlen);
+  const int32_t k0 = c * VA_KEYS;
+  if (k0 >= S) return;  // whole block leaves together
+  const int32_t k1 = min(S, k0 + VA_KEYS);
+  // Thread reads chunk cc (dims 8 cc .. 8 cc + 7) of keys k0 + r, + 16, ...:
+  // sixteen consecutive threads cover one key's 256 bytes.
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, cc = tid & 15, r = tid >> 4;
+  float vm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vm[j] = 0.0f;
+  for (int32_t key = k0 + r; key < k1; key += 128) {
+    u32x4 x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int32_t kk = key + 16 * i;
+      x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (kk < k1) x[i] = v[((int64_t(seg_a) + kk) * n_heads + h) * CHUNKS_PER_ROW + cc];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float f[8];
+      unpack8(x[i], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vm[j] = fmaxf(vm[j], fabsf(f[j]));
+    }
+  }
+  // Over the four threads of the wave with the same chunk, then over the waves.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    vm[j] = fmaxf(vm[j], __shfl_xor(vm[j], 16));
+    vm[j] = fmaxf(vm[j], __shfl_xor(vm[j], 32));
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_red[wv][8 * cc + j] = vm[j];
+  }
+  __syncthreads();
+  if (tid < D) {
+    const float m = fmaxf(fmaxf(s_red[0][tid], s_red[1][tid]), fmaxf(s_red[2][tid], s_red[3][tid]));
+    if (m > 0.0f) atomicMax(v_amax + (int64_t(h) * gridDim.y + s) * D + tid, __float_as_uint(m));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 K/V prologue, keys.  grid = (64-key tiles of the longest segment,
 // segments, heads), 256 threads.
 // k_ws:   [H][rows][128] e4m3 rotated keys, rows past a segment's end zero.
 // k_sc:   [H][rows/64] one word per tile: byte i = 8-bit exponent scale of
 //         keys 16i .. 16i+15.
-// v_amax: [H][n_seqs][128] per value channel, the largest magnitude over the
-//         segment (float bit patterns, which order like the values since they
-//         are >= 0); raised here with atomic max from 0.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __restrict__ k,
-                                                              const u32x4* __restrict__ v,
                                                               const int32_t* __restrict__ cu,
                                                               const float* __restrict__ pos, int32_t n_heads,
                                                               RopeTable tab, u32x2* __restrict__ k_ws,
                                                               unsigned* __restrict__ k_sc,
-                                                              unsigned* __restrict__ v_amax,
                                                               int32_t* __restrict__ order, int64_t rows_per_head,
                                                               int32_t max_seqlen) {
   __shared__ float s_omega[kPairs];
@@ -155,37 +212,6 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
     amax[i] = m;
   }
 
-  // Values: thread owns keys 4 k4 .. 4 k4 + 3 and dims 8 dc .. 8 dc + 7; per
-  // dim the largest magnitude over its keys, then over the 16 threads of the
-  // same dims (lanes that differ in their low four bits).
-  {
-    const int k4 = tid & 15, dc = tid >> 4;
-    float vm[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) vm[j] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = tile * KT + 4 * k4 + i;
-      if (key < S) {
-        float f[8];
-        unpack8(v[((int64_t(seg_a) + key) * n_heads + h) * CHUNKS_PER_ROW + dc], f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vm[j] = fmaxf(vm[j], fabsf(f[j]));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) vm[j] = fmaxf(vm[j], __shfl_xor(vm[j], off));
-    }
-    if (k4 == 0) {
-      unsigned* am = v_amax + (int64_t(h) * gridDim.y + s) * D + 8 * dc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (vm[j] > 0.0f) atomicMax(am + j, __float_as_uint(vm[j]));
-    }
-  }
-
   // Key block maxima over the workgroup.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -221,8 +247,8 @@ __global__ __launch_bounds__(256) void kv_prologue_fp8_kernel(const u32x4* __res
 }
 
 // ---------------------------------------------------------------------------
-// FP8 K/V prologue, pass 2: values.  grid = (64-key tiles, segments, heads),
-// 256 threads, after pass 1 has finished.
+// FP8 K/V prologue, values.  grid = (64-key tiles, segments, heads), 256
+// threads, after v_amax_fp8_kernel has finished.
 // v_ws:   [H][rows/64][128][64] e4m3 values, transposed per tile, keys in the
 //         order v8_key_byte gives, each channel scaled by its segment's
 //         power of two (the exponent e4m3_scale_exponent gives for v_amax).
@@ -276,16 +302,16 @@ __global__ __launch_bounds__(256) void v_quant_fp8_kernel(const u32x4* __restric
 // Online softmax in base 2.  A score MFMA returns s = q8 . k8; the base-2
 // logit is z = cl * s with cl = scale * log2 e, and a probability is stored
 // as p' = exp2(cl * s - mm) = 256 p, where mm is the running reference minus
-// 8 (one multiply-add and one exp2 per element).  Dense instance: the
-// reference moves lazily.  A tile whose lane row sum of p' stays at most 448
-// needs nothing (every p' <= 448); otherwise the wave takes the tile's exact
-// maximum, and only where some p' could pass 448 (the tile's largest logit
-// more than P_ROOM_LOG2 above mm) moves the reference to that maximum,
-// rescales O and l and recomputes the tile.  Skip-Softmax instance: every
-// tile's maximum is taken for the skip rule anyway, so the reference is the
-// exact running maximum.  Either way O and l share one reference, so the
-// result is softmax over the kept keys with P rounded relative to a
-// reference within a factor 1.75 of the running maximum.
+// 8 (one multiply-add and one exp2 per element).  Every tile's maximum is
+// taken before its exponentials: the lane's part from the scores while the
+// previous tile's exponentials run, the row's with one lane swap.  Dense
+// instance: the reference moves lazily, only for rows where some p' could pass
+// 448 (the tile's largest logit more than P_ROOM_LOG2 above mm), to that
+// logit; O and l follow after the previous tile's products.  Skip-Softmax
+// instance: the reference is the exact running maximum of the kept tiles.
+// Either way O and l share one reference, so the result is softmax over the
+// kept keys with P rounded relative to a reference within a factor 1.75 of
+// the running maximum.
 //
 // LDS: rings of eight key slots and eight value slots of 8 KiB.  Iteration t
 // reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+5) and
@@ -446,13 +472,18 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mm = -INFINITY, l = 0.0f;   // reference minus 8, and the row sum of p' = exp2(z - mm)
+  // The factor that takes O and l to this tile's reference, and whether some
+  // row of the wave moved it (wave-uniform).
+  float resc = 1.0f;
+  bool rescale = false;
+  // Dense: the lane's largest raw score of the tile whose exponentials come next.
+  float tmx = -INFINITY;
   // Skip-Softmax: the row's largest base-2 logit over the tiles seen so far, the
   // exponent offset of the current tile (mm, or +inf where the row leaves the
-  // tile out), this tile's rescale factor, and the row's counts.
-  float mt = -INFINITY, moff = 0.0f, resc = 1.0f;
+  // tile out), and the row's counts.
+  float mt = -INFINITY, moff = 0.0f;
   unsigned n_seen = 0, n_skipped = 0;
   bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
-  bool rescale = false;        // Skip-Softmax: some row of the wave moved its reference this tile
   f32x16 sc[2][2];          // S^T of one tile [buffer by tile parity][subtile]
   i32x8 pf[2];              // its e4m3 probabilities, by tile parity
 
@@ -522,16 +553,21 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         sc[b][u][r] = 32 * u + 8 * (r >> 2) + (r & 3) < lim ? x : -INFINITY;
       }
   };
-  // The lane's largest raw score of the tile in buffer B, with its partner's.
-  auto tile_max = [&](auto B) __attribute__((always_inline)) {
+  // The lane's largest raw score of subtile u of the tile in buffer B, of the
+  // whole tile, and of the tile with its partner's (the row's).
+  // Chains of three-operand maxima from a seed (a seed that is itself a
+  // maximum, or -inf, spares the compiler's canonicalizing of raw scores).
+  auto subtile_max = [&](auto B, int u, float seed) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
-    float mx = sc[b][0][0];
+    float mx = seed;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][u][r]);
-    return pair_max(mx);
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[b][u][r]), sc[b][u][r + 1]);
+    return mx;
   };
+  auto lane_max = [&](auto B) __attribute__((always_inline)) {
+    return subtile_max(B, 1, subtile_max(B, 0, -INFINITY));
+  };
+  auto tile_max = [&](auto B) __attribute__((always_inline)) { return pair_max(lane_max(B)); };
   // Unit j (0..7) of tile t's probabilities (scores in buffer B): word j of
   // the lane's 32 bytes, i.e. subtile j / 4, registers 4 (j % 4) .. + 3.
   auto exp_unit = [&](auto B, int j, float (&p)[4]) __attribute__((always_inline)) {
@@ -553,48 +589,33 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     pw[j] = int(w);
     rs = r;
   };
-  // After the exponentials of tile t (buffer B, products of tile t-1 issued).
-  // Dense instance: the rare path that moves the reference, then the row sum.
-  // The first tile always takes it (mm is still -inf there).  Skip-Softmax
-  // instance: the reference was set before the exponentials; here O and l are
-  // rescaled to it (after the products of tile t-1, which used the old one).
-  auto settle = [&](auto B, i32x8& pw, float rs) __attribute__((always_inline)) {
-    constexpr int b = decltype(B)::value;
-    if constexpr (SKIP) {
-      if (rescale) {
+  // After the exponentials of tile t (products of tile t-1 issued): O and l
+  // move to the reference the exponentials used, which prepare (dense) or
+  // decide (Skip-Softmax) set before them, and l takes the tile's row sum.
+  auto settle = [&](float rs) __attribute__((always_inline)) {
+    if (rescale) {
+      l *= resc;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= resc;
-      }
-      l = l * resc + rs;
-    } else {
-      const bool over = !(rs <= E4M3_TOP);  // also true for inf and NaN (the first tile)
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
-        const float tmax = tile_max(ic<b>()) * cl;
-        const bool move = !(tmax - mm <= P_ROOM_LOG2);  // some p' could pass 448 (or mm = -inf)
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
-          const float m_new = move ? fmaxf(mm, tmax - P_SHIFT) : mm;
-          const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf, 1 where unmoved
-          mm = m_new;
-          l *= a;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= a;
-          rs = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cl, -mm));
-            pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
-            rs += (p[0] + p[1]) + (p[2] + p[3]);
-          }
-        }
-      }
-      l += rs;
+        for (int r = 0; r < 16; ++r) o[db][r] *= resc;
+    }
+    l += rs;
+  };
+  // Dense instance, before the exponentials of a tile: move the reference of
+  // the rows where some p' could pass 448 (the tile's largest logit more than
+  // P_ROOM_LOG2 above mm, or mm = -inf on the first tile) to that logit minus
+  // 8.  tmx holds the lane's largest raw score of the tile, taken while the
+  // previous tile's exponentials ran.  O and l follow in settle, after the
+  // products of the previous tile (rounded against the old reference) are in.
+  auto prepare = [&]() __attribute__((always_inline)) {
+    const float tmax = pair_max(tmx) * cl;
+    const bool move = !(tmax - mm <= P_ROOM_LOG2);
+    rescale = __builtin_amdgcn_ballot_w64(move) != 0;
+    if (rescale) {
+      const float m_new = move ? fmaxf(mm, tmax - P_SHIFT) : mm;
+      resc = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf, 1 where unmoved
+      mm = m_new;
     }
   };
 
@@ -603,8 +624,10 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // S(t+1) in the order (subtile, half) = (0,0), (1,0), (0,1), (1,1), straight
   // into sc[1 - B] (consecutive pairs share the query operand); slots 4..7
   // issue O += V(t-1) P(t-1), one MFMA per 32-dim block of O^T (all four
-  // share the probabilities).  Exponential unit j of tile t follows slot j,
-  // then tile t settles.  Two fragment registers alternate, each read one or
+  // share the probabilities).  The dense instance first moves the reference
+  // for tile t (prepare); exponential unit j of tile t follows slot j, the
+  // lane's maximum of S(t+1) is taken in slots 5 and 6, and tile t settles
+  // last.  Two fragment registers alternate, each read one or
   // two slots ahead of its MFMA (the first two at the start).  A scheduling
   // fence after every slot keeps this order.  The Skip-Softmax instance keeps
   // the MFMA order but groups the exponentials: units 0..3 after the score
@@ -625,6 +648,9 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     } else if (do_pv) {
       fr[0] = vfrag(vslot, 0);
       fr[1] = vfrag(vslot, 1);
+    }
+    if constexpr (!SKIP) {
+      if (do_exp) prepare();
     }
     if constexpr (SKIP) {
       // Skip-Softmax instance: the MFMAs of each half, then its exponentials
@@ -701,6 +727,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      float tn = -INFINITY;
   #pragma unroll
       for (int j = 4; j < 8; ++j) {
         if (do_pv) {
@@ -712,11 +739,21 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           exp_unit(ic<b>(), j, p);
           pack_unit(j, p, pw, rs);
         }
+        // The next tile's maximum, subtile 0 then 1, once their score MFMAs
+        // (slots 2 and 3) are done.  The pin keeps the maxima, and so the
+        // score MFMAs, in this block, between the exponentials they overlap
+        // (otherwise the compiler sinks them past the settle branch, next to
+        // the next tile's exponentials, where they serialize).
+        if (do_qk && (j == 5 || j == 6)) {
+          tn = subtile_max(ic<1 - b>(), j - 5, tn);
+          pin(tn);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (do_qk) tmx = tn;
     }
     if (do_exp) {
-      settle(ic<b>(), pw, rs);
+      settle(rs);
       pf[b] = pw;
     }
   };
@@ -777,6 +814,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   auto last = [&](auto B) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     mask_tail(ic<b>(), last_t);
+    if constexpr (!SKIP) tmx = lane_max(ic<b>());  // of the masked scores
     if constexpr (SKIP)
       region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, decide(ic<b>()));
     else
@@ -792,6 +830,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   }
   if (n_kt == 1) {
     mask_tail(ic<0>(), 0);
+    if constexpr (!SKIP) tmx = lane_max(ic<0>());  // of the masked scores
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
     region(ic<0>(), ic<0>(), ic<0>(), true, true, ic<1>(), ic<7>(), 0u, 0u);
     ring_barrier<0>();
@@ -799,6 +838,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   } else {
     ring_barrier<6>();  // every wave is done with K(0) before its slot is refilled
     kscales(1, kq0, kq1);
+    if constexpr (!SKIP) tmx = lane_max(ic<0>());
     // t = 0: no products of an earlier tile yet; an epoch of its own.
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
     region(ic<0>(), ic<1>(), ic<0>(), true, true, ic<1>(), ic<7>(), kq0, kq1);
@@ -882,10 +922,12 @@ int launch_kv_prologue_fp8(const void* k, const void* v, const int32_t* cu, cons
   const int64_t n_amax = int64_t(n_heads) * n_seqs * D;
   const unsigned clear_blocks = unsigned(std::min<int64_t>((n_amax + 255) / 256, 4096));
   hipLaunchKernelGGL(fp8_clear_kernel, dim3(clear_blocks), dim3(256), 0, st, v_amax, n_amax);
+  const unsigned chunks = unsigned((int64_t(max_seqlen) + VA_KEYS - 1) / VA_KEYS);
+  hipLaunchKernelGGL(v_amax_fp8_kernel, dim3(chunks, unsigned(n_seqs), unsigned(n_heads)), dim3(256), 0, st,
+                     static_cast<const u32x4*>(v), cu, n_heads, v_amax, max_seqlen);
   const dim3 grid(tiles, unsigned(n_seqs), unsigned(n_heads));
-  hipLaunchKernelGGL(kv_prologue_fp8_kernel, grid, dim3(256), 0, st, static_cast<const u32x4*>(k),
-                     static_cast<const u32x4*>(v), cu, pos, n_heads, table, static_cast<u32x2*>(k_ws), k_sc, v_amax,
-                     order, rows_per_head, max_seqlen);
+  hipLaunchKernelGGL(kv_prologue_fp8_kernel, grid, dim3(256), 0, st, static_cast<const u32x4*>(k), cu, pos,
+                     n_heads, table, static_cast<u32x2*>(k_ws), k_sc, order, rows_per_head, max_seqlen);
   hipLaunchKernelGGL(v_quant_fp8_kernel, grid, dim3(256), 0, st, static_cast<const u32x4*>(v), cu, n_heads,
                      static_cast<unsigned*>(v_ws), static_cast<const unsigned*>(v_amax), rows_per_head, max_seqlen);
   return int(hipGetLastError());
