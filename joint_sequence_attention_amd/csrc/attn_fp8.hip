@@ -54,6 +54,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 
 #include "device_common.h"
@@ -302,16 +303,16 @@ __global__ __launch_bounds__(256) void v_quant_fp8_kernel(const u32x4* __restric
 // Online softmax in base 2.  A score MFMA returns s = q8 . k8; the base-2
 // logit is z = cl * s with cl = scale * log2 e, and a probability is stored
 // as p' = exp2(cl * s - mm) = 256 p, where mm is the running reference minus
-// 8 (one multiply-add and one exp2 per element).  Every tile's maximum is
-// taken before its exponentials: the lane's part from the scores while the
-// previous tile's exponentials run, the row's with one lane swap.  Dense
-// instance: the reference moves lazily, only for rows where some p' could pass
-// 448 (the tile's largest logit more than P_ROOM_LOG2 above mm), to that
-// logit; O and l follow after the previous tile's products.  Skip-Softmax
-// instance: the reference is the exact running maximum of the kept tiles.
-// Either way O and l share one reference, so the result is softmax over the
-// kept keys with P rounded relative to a reference within a factor 1.75 of
-// the running maximum.
+// 8 (one multiply-add and one exp2 per element).  Dense instance: the
+// reference moves lazily.  A tile none of whose packed probabilities reached
+// 448 needs nothing; otherwise the wave takes the tile's exact maximum, and
+// only where some p' could pass 448 (the tile's largest logit more than
+// P_ROOM_LOG2 above mm) moves the reference to that maximum, rescales O and l
+// and recomputes the tile.  Skip-Softmax instance: every tile's maximum is
+// taken for the skip rule anyway, so the reference is the exact running
+// maximum of the kept tiles.  Either way O and l share one reference, so the
+// result is softmax over the kept keys with P rounded relative to a reference
+// within a factor 1.75 of the running maximum.
 //
 // LDS: rings of eight key slots and eight value slots of 8 KiB.  Iteration t
 // reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+5) and
@@ -472,16 +473,12 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mm = -INFINITY, l = 0.0f;   // reference minus 8, and the row sum of p' = exp2(z - mm)
-  // The factor that takes O and l to this tile's reference, and whether some
-  // row of the wave moved it (wave-uniform).
-  float resc = 1.0f;
-  bool rescale = false;
-  // Dense: the lane's largest raw score of the tile whose exponentials come next.
-  float tmx = -INFINITY;
   // Skip-Softmax: the row's largest base-2 logit over the tiles seen so far, the
   // exponent offset of the current tile (mm, or +inf where the row leaves the
-  // tile out), and the row's counts.
-  float mt = -INFINITY, moff = 0.0f;
+  // tile out), this tile's rescale factor, whether some row of the wave moved
+  // its reference this tile (wave-uniform), and the row's counts.
+  float mt = -INFINITY, moff = 0.0f, resc = 1.0f;
+  bool rescale = false;
   unsigned n_seen = 0, n_skipped = 0;
   bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
   f32x16 sc[2][2];          // S^T of one tile [buffer by tile parity][subtile]
@@ -589,33 +586,57 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     pw[j] = int(w);
     rs = r;
   };
-  // After the exponentials of tile t (products of tile t-1 issued): O and l
-  // move to the reference the exponentials used, which prepare (dense) or
-  // decide (Skip-Softmax) set before them, and l takes the tile's row sum.
-  auto settle = [&](float rs) __attribute__((always_inline)) {
-    if (rescale) {
-      l *= resc;
+  // After the exponentials of tile t (buffer B, products of tile t-1 issued),
+  // with chk the OR over the lane's packed words of (word + 0x02020202).
+  // Dense instance: every p' <= 448 rounds to at most 0x7e and an overflow
+  // gives 0x7f (an e4m3 NaN), so a byte at 0x7e or above, i.e. bit 7 set in
+  // chk, flags a p' that reached 448; a NaN gives 0xff, whose carry spoils the
+  // test, but then the row sum is NaN or infinite too.  Only a flagged wave
+  // takes the tile's exact maximum, and only where some p' could pass 448
+  // (the tile's largest logit more than P_ROOM_LOG2 above mm) does it move the
+  // reference to that maximum, rescale O and l and recompute the tile.  The
+  // first tile always takes this path (mm is still -inf there).  Skip-Softmax
+  // instance: the reference was set before the exponentials; here O and l
+  // are rescaled to it (after the products of tile t-1, which used the old
+  // one).
+  auto settle = [&](auto B, i32x8& pw, float rs, unsigned chk) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    if constexpr (SKIP) {
+      (void)chk;
+      if (rescale) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= resc;
-    }
-    l += rs;
-  };
-  // Dense instance, before the exponentials of a tile: move the reference of
-  // the rows where some p' could pass 448 (the tile's largest logit more than
-  // P_ROOM_LOG2 above mm, or mm = -inf on the first tile) to that logit minus
-  // 8.  tmx holds the lane's largest raw score of the tile, taken while the
-  // previous tile's exponentials ran.  O and l follow in settle, after the
-  // products of the previous tile (rounded against the old reference) are in.
-  auto prepare = [&]() __attribute__((always_inline)) {
-    const float tmax = pair_max(tmx) * cl;
-    const bool move = !(tmax - mm <= P_ROOM_LOG2);
-    rescale = __builtin_amdgcn_ballot_w64(move) != 0;
-    if (rescale) {
-      const float m_new = move ? fmaxf(mm, tmax - P_SHIFT) : mm;
-      resc = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf, 1 where unmoved
-      mm = m_new;
+          for (int r = 0; r < 16; ++r) o[db][r] *= resc;
+      }
+      l = l * resc + rs;
+    } else {
+      const bool over = (chk & 0x80808080u) != 0u || !(rs <= FLT_MAX);
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        const float tmax = tile_max(ic<b>()) * cl;
+        const bool move = !(tmax - mm <= P_ROOM_LOG2);  // some p' could pass 448 (or mm = -inf)
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float m_new = move ? fmaxf(mm, tmax - P_SHIFT) : mm;
+          const float a = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf, 1 where unmoved
+          mm = m_new;
+          l *= a;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= a;
+          rs = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][j >> 2][4 * (j & 3) + i], cl, -mm));
+            pw[j] = int(pack_e4m3x4(p[0], p[1], p[2], p[3]));
+            rs += (p[0] + p[1]) + (p[2] + p[3]);
+          }
+        }
+      }
+      l += rs;
     }
   };
 
@@ -624,10 +645,8 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // S(t+1) in the order (subtile, half) = (0,0), (1,0), (0,1), (1,1), straight
   // into sc[1 - B] (consecutive pairs share the query operand); slots 4..7
   // issue O += V(t-1) P(t-1), one MFMA per 32-dim block of O^T (all four
-  // share the probabilities).  The dense instance first moves the reference
-  // for tile t (prepare); exponential unit j of tile t follows slot j, the
-  // lane's maximum of S(t+1) is taken in slots 5 and 6, and tile t settles
-  // last.  Two fragment registers alternate, each read one or
+  // share the probabilities).  Exponential unit j of tile t follows slot j,
+  // then tile t settles.  Two fragment registers alternate, each read one or
   // two slots ahead of its MFMA (the first two at the start).  A scheduling
   // fence after every slot keeps this order.  The Skip-Softmax instance keeps
   // the MFMA order but groups the exponentials: units 0..3 after the score
@@ -648,9 +667,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     } else if (do_pv) {
       fr[0] = vfrag(vslot, 0);
       fr[1] = vfrag(vslot, 1);
-    }
-    if constexpr (!SKIP) {
-      if (do_exp) prepare();
     }
     if constexpr (SKIP) {
       // Skip-Softmax instance: the MFMAs of each half, then its exponentials
@@ -727,7 +743,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      float tn = -INFINITY;
   #pragma unroll
       for (int j = 4; j < 8; ++j) {
         if (do_pv) {
@@ -739,21 +754,22 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           exp_unit(ic<b>(), j, p);
           pack_unit(j, p, pw, rs);
         }
-        // The next tile's maximum, subtile 0 then 1, once their score MFMAs
-        // (slots 2 and 3) are done.  The pin keeps the maxima, and so the
-        // score MFMAs, in this block, between the exponentials they overlap
-        // (otherwise the compiler sinks them past the settle branch, next to
-        // the next tile's exponentials, where they serialize).
-        if (do_qk && (j == 5 || j == 6)) {
-          tn = subtile_max(ic<1 - b>(), j - 5, tn);
-          pin(tn);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (do_qk) tmx = tn;
+      // A use of S(t+1) here keeps its MFMAs in this block, between the
+      // exponentials they overlap: otherwise the compiler sinks them past the
+      // settle branch, next to the next tile's exponentials, where they run
+      // back to back and the exponentials wait for them.  They are done by
+      // now, so the use waits for nothing.
+      if (do_qk) asm volatile("" ::"v"(sc[1 - b][0]), "v"(sc[1 - b][1]));
     }
     if (do_exp) {
-      settle(rs);
+      unsigned chk = 0u;
+      if constexpr (!SKIP) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) chk |= unsigned(pw[j]) + 0x02020202u;
+      }
+      settle(ic<b>(), pw, rs, chk);
       pf[b] = pw;
     }
   };
@@ -814,7 +830,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   auto last = [&](auto B) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     mask_tail(ic<b>(), last_t);
-    if constexpr (!SKIP) tmx = lane_max(ic<b>());  // of the masked scores
     if constexpr (SKIP)
       region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, decide(ic<b>()));
     else
@@ -830,7 +845,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   }
   if (n_kt == 1) {
     mask_tail(ic<0>(), 0);
-    if constexpr (!SKIP) tmx = lane_max(ic<0>());  // of the masked scores
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
     region(ic<0>(), ic<0>(), ic<0>(), true, true, ic<1>(), ic<7>(), 0u, 0u);
     ring_barrier<0>();
@@ -838,7 +852,6 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   } else {
     ring_barrier<6>();  // every wave is done with K(0) before its slot is refilled
     kscales(1, kq0, kq1);
-    if constexpr (!SKIP) tmx = lane_max(ic<0>());
     // t = 0: no products of an earlier tile yet; an epoch of its own.
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
     region(ic<0>(), ic<1>(), ic<0>(), true, true, ic<1>(), ic<7>(), kq0, kq1);
