@@ -55,7 +55,9 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 N_XCD = 8                  # GRBM_GUI_ACTIVE is summed over the XCDs
 SIMDS_PER_CU = 4
-KERNELS = {"bf16": "attn_fwd_kernel(", "fp8": "attn_fwd_fp8_kernel<false>"}
+# Kernel names as rocprofv3 prints them; the FP8 pattern takes both dense instances (the launch
+# picks one by the longest segment) and leaves out the Skip-Softmax one.
+KERNELS = {"bf16": "attn_fwd_kernel(", "fp8": "attn_fwd_fp8_kernel<false,"}
 
 
 def _find_csv(d, suffix):

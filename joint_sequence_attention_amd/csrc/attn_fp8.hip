@@ -79,6 +79,13 @@ constexpr float E4M3_TOP = 448.0f;       // largest finite e4m3 value
 // room for the rounding of the exponent's argument.
 constexpr float P_ROOM_LOG2 = 8.75f;
 constexpr int E8M0_ONE = 127;            // 8-bit exponent scale of 2^0
+// The dense instance moves its reference in one of two ways (see the kernel):
+// early, from each tile's maximum taken before its exponentials, or late,
+// after a test of the packed probabilities.  On N(0, 1)-like logits the
+// reference of some row of a wave moves on about 26 % of tiles at 8K keys
+// and 3 % at 130K keys; the late form is cheaper per tile and dearer per
+// move, and wins from about this many keys per segment.
+constexpr int32_t F8_LATE_MIN_KEYS = 65536;
 
 // LDS layouts, XOR-swizzled so that the 16-byte fragment reads of a wave hit
 // distinct banks (SQ_LDS_BANK_CONFLICT reads 0 for both access patterns on
@@ -304,13 +311,17 @@ __global__ __launch_bounds__(256) void v_quant_fp8_kernel(const u32x4* __restric
 // logit is z = cl * s with cl = scale * log2 e, and a probability is stored
 // as p' = exp2(cl * s - mm) = 256 p, where mm is the running reference minus
 // 8 (one multiply-add and one exp2 per element).  Dense instance: the
-// reference moves lazily.  A tile none of whose packed probabilities reached
-// 448 needs nothing; otherwise the wave takes the tile's exact maximum, and
-// only where some p' could pass 448 (the tile's largest logit more than
-// P_ROOM_LOG2 above mm) moves the reference to that maximum, rescales O and l
-// and recomputes the tile.  Skip-Softmax instance: every tile's maximum is
-// taken for the skip rule anyway, so the reference is the exact running
-// maximum of the kept tiles.  Either way O and l share one reference, so the
+// reference moves lazily, only where some p' could pass 448 (the tile's
+// largest logit more than P_ROOM_LOG2 above mm), to that logit, in one of two
+// forms chosen per launch by the longest segment.  Early (shorter segments,
+// where moves are frequent): every tile's maximum is taken before its
+// exponentials, the lane's part while the previous tile's exponentials run,
+// and O and l follow after the previous tile's products.  Late (long
+// segments): a tile none of whose packed probabilities reached 448 needs
+// nothing; otherwise the wave takes the tile's exact maximum, moves the
+// reference where needed, rescales O and l and recomputes the tile.
+// Skip-Softmax instance: every tile's maximum is taken for the skip rule
+// anyway, so the reference is the exact running maximum of the kept tiles.  Either way O and l share one reference, so the
 // result is softmax over the kept keys with P rounded relative to a reference
 // within a factor 1.75 of the running maximum.
 //
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(256) void v_quant_fp8_kernel(const u32x4* __restric
 // V(t+3); iterations pair up into epochs that end with one barrier, exactly
 // as in the bf16 kernel.
 // ---------------------------------------------------------------------------
-template <bool SKIP>
+template <bool SKIP, bool LATE>
 __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     const u32x4* __restrict__ q, const int32_t* __restrict__ cu, const float* __restrict__ pos,
     u32x2* __restrict__ out, float* __restrict__ lse, int32_t n_tokens, int32_t n_heads, float scale_log2,
@@ -473,12 +484,18 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float mm = -INFINITY, l = 0.0f;   // reference minus 8, and the row sum of p' = exp2(z - mm)
+  // The factor that takes O and l to this tile's reference, and whether some
+  // row of the wave moved it (wave-uniform): Skip-Softmax and the early dense
+  // form.
+  float resc = 1.0f;
+  bool rescale = false;
+  // Early dense form: the lane's largest raw score of the tile whose
+  // exponentials come next.
+  float tmx = -INFINITY;
   // Skip-Softmax: the row's largest base-2 logit over the tiles seen so far, the
   // exponent offset of the current tile (mm, or +inf where the row leaves the
-  // tile out), this tile's rescale factor, whether some row of the wave moved
-  // its reference this tile (wave-uniform), and the row's counts.
-  float mt = -INFINITY, moff = 0.0f, resc = 1.0f;
-  bool rescale = false;
+  // tile out), and the row's counts.
+  float mt = -INFINITY, moff = 0.0f;
   unsigned n_seen = 0, n_skipped = 0;
   bool prev_kept = true;       // Skip-Softmax: the wave kept the previous tile (wave-uniform)
   f32x16 sc[2][2];          // S^T of one tile [buffer by tile parity][subtile]
@@ -588,7 +605,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   };
   // After the exponentials of tile t (buffer B, products of tile t-1 issued),
   // with chk the OR over the lane's packed words of (word + 0x02020202).
-  // Dense instance: every p' <= 448 rounds to at most 0x7e and an overflow
+  // Late dense form: every p' <= 448 rounds to at most 0x7e and an overflow
   // gives 0x7f (an e4m3 NaN), so a byte at 0x7e or above, i.e. bit 7 set in
   // chk, flags a p' that reached 448; a NaN gives 0xff, whose carry spoils the
   // test, but then the row sum is NaN or infinite too.  Only a flagged wave
@@ -596,20 +613,21 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // (the tile's largest logit more than P_ROOM_LOG2 above mm) does it move the
   // reference to that maximum, rescale O and l and recompute the tile.  The
   // first tile always takes this path (mm is still -inf there).  Skip-Softmax
-  // instance: the reference was set before the exponentials; here O and l
-  // are rescaled to it (after the products of tile t-1, which used the old
-  // one).
+  // instance and early dense form: the reference was set before the
+  // exponentials (decide, prepare); here O and l are rescaled to it (after
+  // the products of tile t-1, which used the old one).
   auto settle = [&](auto B, i32x8& pw, float rs, unsigned chk) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
-    if constexpr (SKIP) {
+    if constexpr (SKIP || !LATE) {
       (void)chk;
       if (rescale) {
+        l *= resc;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][r] *= resc;
       }
-      l = l * resc + rs;
+      l += rs;
     } else {
       const bool over = (chk & 0x80808080u) != 0u || !(rs <= FLT_MAX);
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
@@ -640,6 +658,22 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     }
   };
 
+  // Early dense form, before the exponentials of a tile: move the reference of
+  // the rows where some p' could pass 448 (the tile's largest logit more than
+  // P_ROOM_LOG2 above mm, or mm = -inf on the first tile) to that logit minus
+  // 8.  tmx holds the lane's largest raw score of the tile, taken while the
+  // previous tile's exponentials ran.  O and l follow in settle.
+  auto prepare = [&]() __attribute__((always_inline)) {
+    const float tmax = pair_max(tmx) * cl;
+    const bool move = !(tmax - mm <= P_ROOM_LOG2);
+    rescale = __builtin_amdgcn_ballot_w64(move) != 0;
+    if (rescale) {
+      const float m_new = move ? fmaxf(mm, tmax - P_SHIFT) : mm;
+      resc = __builtin_amdgcn_exp2f(mm - m_new);  // 0 from mm = -inf, 1 where unmoved
+      mm = m_new;
+    }
+  };
+
   // Iteration t, B = t mod 2 (S(t) in sc[B], P(t-1) in pf[1 - B]), reading
   // K(t+1) from kslot and V(t-1) from vslot: 8 MFMA slots.  Slots 0..3 issue
   // S(t+1) in the order (subtile, half) = (0,0), (1,0), (0,1), (1,1), straight
@@ -667,6 +701,9 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
     } else if (do_pv) {
       fr[0] = vfrag(vslot, 0);
       fr[1] = vfrag(vslot, 1);
+    }
+    if constexpr (!SKIP && !LATE) {
+      if (do_exp) prepare();
     }
     if constexpr (SKIP) {
       // Skip-Softmax instance: the MFMAs of each half, then its exponentials
@@ -743,6 +780,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      float tn = -INFINITY;
   #pragma unroll
       for (int j = 4; j < 8; ++j) {
         if (do_pv) {
@@ -754,18 +792,31 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
           exp_unit(ic<b>(), j, p);
           pack_unit(j, p, pw, rs);
         }
+        // Early form: the next tile's maximum, subtile 0 then 1, once their
+        // score MFMAs (slots 2 and 3) are done.
+        if constexpr (!LATE) {
+          if (do_qk && (j == 5 || j == 6)) {
+            tn = subtile_max(ic<1 - b>(), j - 5, tn);
+            pin(tn);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // A use of S(t+1) here keeps its MFMAs in this block, between the
-      // exponentials they overlap: otherwise the compiler sinks them past the
-      // settle branch, next to the next tile's exponentials, where they run
-      // back to back and the exponentials wait for them.  They are done by
-      // now, so the use waits for nothing.
-      if (do_qk) asm volatile("" ::"v"(sc[1 - b][0]), "v"(sc[1 - b][1]));
+      // A use of S(t+1) in this block (the early form's maximum, the late
+      // form's empty asm) keeps its MFMAs here, between the exponentials they
+      // overlap: otherwise the compiler sinks them past the settle branch,
+      // next to the next tile's exponentials, where they run back to back and
+      // the exponentials wait for them.  They are done by now, so the use
+      // waits for nothing.
+      if constexpr (LATE) {
+        if (do_qk) asm volatile("" ::"v"(sc[1 - b][0]), "v"(sc[1 - b][1]));
+      } else {
+        if (do_qk) tmx = tn;
+      }
     }
     if (do_exp) {
       unsigned chk = 0u;
-      if constexpr (!SKIP) {
+      if constexpr (!SKIP && LATE) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) chk |= unsigned(pw[j]) + 0x02020202u;
       }
@@ -830,6 +881,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   auto last = [&](auto B) __attribute__((always_inline)) {
     constexpr int b = decltype(B)::value;
     mask_tail(ic<b>(), last_t);
+    if constexpr (!SKIP && !LATE) tmx = lane_max(ic<b>());  // of the masked scores
     if constexpr (SKIP)
       region_skip(ic<b>(), ic<0>(), 0, (last_t - 1) & 7, kq0, kq1, decide(ic<b>()));
     else
@@ -845,6 +897,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   }
   if (n_kt == 1) {
     mask_tail(ic<0>(), 0);
+    if constexpr (!SKIP && !LATE) tmx = lane_max(ic<0>());  // of the masked scores
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
     region(ic<0>(), ic<0>(), ic<0>(), true, true, ic<1>(), ic<7>(), 0u, 0u);
     ring_barrier<0>();
@@ -852,6 +905,7 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   } else {
     ring_barrier<6>();  // every wave is done with K(0) before its slot is refilled
     kscales(1, kq0, kq1);
+    if constexpr (!SKIP && !LATE) tmx = lane_max(ic<0>());
     // t = 0: no products of an earlier tile yet; an epoch of its own.
     if constexpr (SKIP) (void)decide(ic<0>());  // the first tile is always kept: this sets the reference
     region(ic<0>(), ic<1>(), ic<0>(), true, true, ic<1>(), ic<7>(), kq0, kq1);
@@ -954,34 +1008,43 @@ int launch_attention_fp8(const void* q, const int32_t* cu, const float* pos, voi
   const unsigned tiles = unsigned((int64_t(max_seqlen) + F8_BQ - 1) / F8_BQ);
   if (tiles == 0) return 0;
   const bool skip = skip_threshold > 0.0f;
-  const void* fn = skip ? reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<true>)
-                        : reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<false>);
+  const bool late = !skip && max_seqlen >= F8_LATE_MIN_KEYS;
+  const int inst = skip ? 2 : late ? 1 : 0;
+  const void* fn = skip   ? reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<true, false>)
+                   : late ? reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<false, true>)
+                          : reinterpret_cast<const void*>(&attn_fwd_fp8_kernel<false, false>);
   // The dynamic LDS limit is raised once per device and kernel instance.
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return int(e);
-  static std::atomic<uint64_t> attr_set[2] = {0, 0};
+  static std::atomic<uint64_t> attr_set[3] = {0, 0, 0};
   const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
-  if (bit == 0 || (attr_set[skip].load(std::memory_order_acquire) & bit) == 0) {
+  if (bit == 0 || (attr_set[inst].load(std::memory_order_acquire) & bit) == 0) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(F8_SMEM));
     if (e != hipSuccess) return int(e);
-    attr_set[skip].fetch_or(bit, std::memory_order_acq_rel);
+    attr_set[inst].fetch_or(bit, std::memory_order_acq_rel);
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   const float skip_log2 = skip ? std::log2(skip_threshold) : 0.0f;
   // Grid (query tile, head, segment rank): the longest segments go first.
   const dim3 grid(tiles, unsigned(n_heads), unsigned(n_seqs));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* q4 = static_cast<const u32x4*>(q);
+  u32x2* o2 = static_cast<u32x2*>(out);
+  const char* kc = static_cast<const char*>(k_ws);
+  const char* vc = static_cast<const char*>(v_ws);
   if (skip)
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, grid, dim3(F8_NW * 64), F8_SMEM, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4*>(q), cu, pos, static_cast<u32x2*>(out), lse, int32_t(n_tokens),
-                       n_heads, scale_log2, table, static_cast<const char*>(k_ws), static_cast<const char*>(v_ws),
-                       k_sc, v_amax, order, rows_per_head, max_seqlen, skip_log2, skip_stats);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, false>), grid, dim3(F8_NW * 64), F8_SMEM, st, q4, cu, pos, o2, lse,
+                       int32_t(n_tokens), n_heads, scale_log2, table, kc, vc, k_sc, v_amax, order, rows_per_head,
+                       max_seqlen, skip_log2, skip_stats);
+  else if (late)
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, true>), grid, dim3(F8_NW * 64), F8_SMEM, st, q4, cu, pos, o2, lse,
+                       int32_t(n_tokens), n_heads, scale_log2, table, kc, vc, k_sc, v_amax, order, rows_per_head,
+                       max_seqlen, 0.0f, nullptr);
   else
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, grid, dim3(F8_NW * 64), F8_SMEM,
-                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(q), cu, pos,
-                       static_cast<u32x2*>(out), lse, int32_t(n_tokens), n_heads, scale_log2, table,
-                       static_cast<const char*>(k_ws), static_cast<const char*>(v_ws), k_sc, v_amax, order,
-                       rows_per_head, max_seqlen, 0.0f, nullptr);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, false>), grid, dim3(F8_NW * 64), F8_SMEM, st, q4, cu, pos, o2, lse,
+                       int32_t(n_tokens), n_heads, scale_log2, table, kc, vc, k_sc, v_amax, order, rows_per_head,
+                       max_seqlen, 0.0f, nullptr);
   return int(hipGetLastError());
 }
 

@@ -81,9 +81,10 @@ class Case:
         torch.cuda.synchronize()
         return out, lse
 
-    def run_fp8(self, **kw):
+    def run_fp8(self, max_seqlen=None, **kw):
         import torch
-        out, lse = H.h3attn_varlen_fwd_fp8(self.q, self.k, self.v, self.cu_d, self.pos_d, self.max_seqlen, **kw)
+        ms = self.max_seqlen if max_seqlen is None else max_seqlen
+        out, lse = H.h3attn_varlen_fwd_fp8(self.q, self.k, self.v, self.cu_d, self.pos_d, ms, **kw)
         torch.cuda.synchronize()
         return out, lse
 

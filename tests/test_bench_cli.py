@@ -23,7 +23,10 @@ def test_counter_csv_parsing_and_derived_fields(tmp_path):
     for d in range(3):
         rows.append(f'{d},"h3attn::(anonymous namespace)::attn_fwd_kernel(int)",SQ_VALU_MFMA_BUSY_CYCLES,{4.0e10 + d}')
         rows.append(f'{d},"h3attn::(anonymous namespace)::attn_fwd_kernel(int)",GRBM_GUI_ACTIVE,4.8e8')
-        rows.append(f'{d},"void h3attn::(anonymous namespace)::attn_fwd_fp8_kernel<false>(int)",FETCH_SIZE,1000')
+        rows.append(f'{d},"void h3attn::(anonymous namespace)::attn_fwd_fp8_kernel<false, {"true" if d else "false"}>(int)",'
+                    'FETCH_SIZE,1000')
+        # the Skip-Softmax instance is not the dense kernel the FP8 line reports
+        rows.append(f'{d},"void h3attn::(anonymous namespace)::attn_fwd_fp8_kernel<true, false>(int)",FETCH_SIZE,9')
         rows.append(f'{d},"h3attn::(anonymous namespace)::kv_prologue_kernel(int)",FETCH_SIZE,7')
     cc.write_text("\n".join(rows) + "\n")
     c = bench.parse_counter_csv(str(cc))

@@ -25,36 +25,68 @@ from joint_sequence_attention_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
+# The dense kernel moves its softmax reference in one of two forms, chosen per launch by
+# max_seqlen: early below 65,536 keys, late from there on.  The small cases run in both: for the
+# late form one 65,536-token segment follows them in the same launch, and only their own rows
+# are compared (the long segment's rows are checked for being finite).
+FORMS = ["early", "late"]
+FILLER = [wl.visual(16, 64, 64)]  # 65,536 tokens
 
-def _full(c, label, exact_bars=True, scale=None, **kw):
-    out, lse = c.run_fp8(softmax_scale=scale or 0.0, **kw)
-    o_s, l_s, es = c.sage_rows(scale=scale, **kw)
-    o_e, l_e = c.oracle_full(scale=scale, **kw)
-    return compare_fp8(device_to_f64(out), device_to_f64(lse), o_s, l_s, es, o_e, l_e, label=label,
-                       exact_bars=exact_bars)
+
+def _segments(segments, form):
+    return list(segments) + [FILLER] if form == "late" else list(segments)
 
 
+def _n_rows(c, n_segments):
+    """Rows of the first n_segments segments of a case."""
+    return int(c.cu[n_segments])
+
+
+def _full(c, label, exact_bars=True, scale=None, n_rows=None, max_seqlen=None, **kw):
+    out, lse = c.run_fp8(max_seqlen=max_seqlen, softmax_scale=scale or 0.0, **kw)
+    out64, lse64 = device_to_f64(out), device_to_f64(lse)
+    if n_rows is None or n_rows == c.N:
+        o_s, l_s, es = c.sage_rows(scale=scale, **kw)
+        o_e, l_e = c.oracle_full(scale=scale, **kw)
+    else:
+        assert np.all(np.isfinite(out64[n_rows:])) and np.all(np.isfinite(lse64[:, n_rows:]))
+        rows = np.arange(n_rows)
+        o_s, l_s, es = c.sage_rows(rows, scale=scale, **kw)
+        o_e, l_e = c.oracle_rows(rows, scale=scale, **kw)
+        out64, lse64 = out64[:n_rows], lse64[:, :n_rows]
+    return compare_fp8(out64, lse64, o_s, l_s, es, o_e, l_e, label=label, exact_bars=exact_bars)
+
+
+def _form_case(segments, heads, seed, form, **kw):
+    """(case, rows to compare) for the small segments in the given form."""
+    c = Case(_segments(segments, form), heads, seed, **kw)
+    return c, _n_rows(c, len(segments))
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("seed", [1, 1001])
-def test_fp8_tiny_full(gpu, seed):
+def test_fp8_tiny_full(gpu, seed, form):
     cfg = wl.config("tiny")
-    c = Case(cfg["segments"], cfg["heads"], seed)
-    say(f"fp8 tiny seed {seed}: N={c.N} H={c.heads}")
-    _full(c, f"tiny/{seed}")
+    c, n = _form_case(cfg["segments"], cfg["heads"], seed, form)
+    say(f"fp8 tiny seed {seed} ({form}): N={c.N} H={c.heads}")
+    _full(c, f"tiny/{seed}/{form}", n_rows=n)
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("heads", [1, 3])
-def test_fp8_ragged_segments_full(gpu, heads):
-    c = Case(ragged_segments(), heads, 140 + heads)
-    say(f"fp8 ragged: lens={c.lens.tolist()} H={heads}")
-    _full(c, "ragged")
+def test_fp8_ragged_segments_full(gpu, heads, form):
+    c, n = _form_case(ragged_segments(), heads, 140 + heads, form)
+    say(f"fp8 ragged ({form}): lens={c.lens.tolist()} H={heads}")
+    _full(c, f"ragged/{form}", n_rows=n)
 
 
-def test_fp8_peaky_softmax_full(gpu):
+@pytest.mark.parametrize("form", FORMS)
+def test_fp8_peaky_softmax_full(gpu, form):
     # q x 4: logits four times wider; checked against the quantized oracle (the
     # distance from exact softmax grows with the logits and is only reported).
-    c = Case(ragged_segments(), 2, 150, qscale=4.0)
-    say(f"fp8 peaky: lens={c.lens.tolist()}")
-    _full(c, "peaky", exact_bars=False)
+    c, n = _form_case(ragged_segments(), 2, 150, form, qscale=4.0)
+    say(f"fp8 peaky ({form}): lens={c.lens.tolist()}")
+    _full(c, f"peaky/{form}", exact_bars=False, n_rows=n)
 
 
 @pytest.mark.parametrize("name", ["480p", "packed", "1344x768", "ref2va", "long300"])
@@ -74,10 +106,11 @@ def test_fp8_workload_sampled_rows(gpu, name, seed_offset):
                 label=f"{name}/{seed} ({len(rows)} rows, every query tile)")
 
 
-def test_fp8_explicit_scale_and_rope_config(gpu):
-    c = Case(ragged_segments(), 2, 164)
-    say("fp8 explicit scale / rope config")
-    _full(c, "scale/theta", scale=0.05, theta=500.0, dims=(64, 32, 32))
+@pytest.mark.parametrize("form", FORMS)
+def test_fp8_explicit_scale_and_rope_config(gpu, form):
+    c, n = _form_case(ragged_segments(), 2, 164, form)
+    say(f"fp8 explicit scale / rope config ({form})")
+    _full(c, f"scale/theta/{form}", scale=0.05, theta=500.0, dims=(64, 32, 32), n_rows=n)
 
 
 def test_fp8_two_stages_equal_fused_call_and_deterministic(gpu):
@@ -110,15 +143,11 @@ def test_fp8_segment_isolation_bitwise(gpu):
         assert np.array_equal(lse[:, a:b].cpu().numpy(), l1.cpu().numpy())
 
 
-def test_fp8_length_one_and_empty_segments(gpu):
-    import torch
+@pytest.mark.parametrize("form", FORMS)
+def test_fp8_length_one_and_empty_segments(gpu, form):
     segs = [[], [wl.visual(1, 1, 1)], [], [wl.audio(1, 1.0, attached=False)], [wl.visual(1, 5, 7)], []]
-    c = Case(segs, 2, 166)
-    out, lse = H.h3attn_varlen_fwd_fp8(c.q, c.k, c.v, c.cu_d, c.pos_d, c.N)  # generous max_seqlen
-    torch.cuda.synchronize()
-    o_s, l_s, es = c.sage_rows()
-    o_e, l_e = c.oracle_full()
-    compare_fp8(device_to_f64(out), device_to_f64(lse), o_s, l_s, es, o_e, l_e, label="length-1/empty")
+    c, n = _form_case(segs, 2, 166, form)
+    _full(c, f"length-1/empty/{form}", n_rows=n, max_seqlen=c.N)  # generous max_seqlen
 
 
 def test_fp8_zero_tokens_noop(gpu):
@@ -163,11 +192,12 @@ def test_fp8_many_heads_full(gpu):
     _full(c, "128 heads")
 
 
-def test_fp8_refiner_full(gpu):
+@pytest.mark.parametrize("form", FORMS)
+def test_fp8_refiner_full(gpu, form):
     cfg = wl.config("refiner")
-    c = Case(cfg["segments"], cfg["heads"], cfg["seed"])
-    say(f"fp8 refiner: N={c.N} H={c.heads}")
-    _full(c, "refiner")
+    c, n = _form_case(cfg["segments"], cfg["heads"], cfg["seed"], form)
+    say(f"fp8 refiner ({form}): N={c.N} H={c.heads}")
+    _full(c, f"refiner/{form}", n_rows=n)
 
 
 # ---- Skip-Softmax ------------------------------------------------------------------------------
@@ -309,10 +339,11 @@ def test_fp8_skip_timed_workload_head0_counts(gpu):
 # ---- Running maximum that moves on every tile ----------------------------------------------------
 
 
-def _rising_case(n_tokens, heads, seed, top=40.0):
+def _rising_case(n_tokens, heads, seed, top=40.0, form=None):
     """Keys that line up with the queries and grow along the sequence: every 64-key tile holds
     larger logits than the one before, so the running maximum moves on every tile (up to ~top
-    natural units), with ragged segment lengths."""
+    natural units), with ragged segment lengths.  With a form, returns (case, rows of these
+    segments), the late form's long segment after them with N(0, 1) rows."""
     from helpers import bits_to_device
     rng = np.random.default_rng(seed)
     c = rng.standard_normal((heads, 128))
@@ -325,24 +356,30 @@ def _rising_case(n_tokens, heads, seed, top=40.0):
     def bits(x):
         return wl._round_bf16_bits(np.ascontiguousarray(x, dtype=np.float32))
     lens = [1, 63, 64, 65, 200, n_tokens - 393]
-    c0 = Case([[wl.visual(1, 1, n)] for n in lens], heads, seed)
+    segs = [[wl.visual(1, 1, n)] for n in lens]
+    c0 = Case(_segments(segs, form), heads, seed)
+    extra = c0.N - n_tokens
+    if extra:
+        q, k, v = (np.concatenate([x, rng.standard_normal((extra, heads, 128))]) for x in (q, k, v))
     c0.qb, c0.kb, c0.vb = bits(q), bits(k), bits(v)
     dev = c0.q.device
     c0.q, c0.k, c0.v = bits_to_device(c0.qb, dev), bits_to_device(c0.kb, dev), bits_to_device(c0.vb, dev)
-    return c0
+    return c0 if form is None else (c0, n_tokens)
 
 
-def test_fp8_running_maximum_moves_every_tile(gpu):
-    c = _rising_case(1200, 2, 190)
-    say(f"fp8 rising logits: lens={c.lens.tolist()}")
-    _full(c, "rising", exact_bars=False)
+@pytest.mark.parametrize("form", FORMS)
+def test_fp8_running_maximum_moves_every_tile(gpu, form):
+    c, n = _rising_case(1200, 2, 190, form=form)
+    say(f"fp8 rising logits ({form}): lens={c.lens.tolist()}")
+    _full(c, f"rising/{form}", exact_bars=False, n_rows=n)
 
 
-def test_fp8_very_large_logits(gpu):
+@pytest.mark.parametrize("form", FORMS)
+def test_fp8_very_large_logits(gpu, form):
     # q x 64: logits of several hundred, far past exp2's range without a reference; every row
     # must still come out finite and match the oracle
-    c = Case(ragged_segments(), 2, 191, qscale=64.0)
-    say(f"fp8 very large logits: lens={c.lens.tolist()}")
+    c, n = _form_case(ragged_segments(), 2, 191, form, qscale=64.0)
+    say(f"fp8 very large logits ({form}): lens={c.lens.tolist()}")
     out, lse = c.run_fp8()
     assert np.all(np.isfinite(device_to_f64(out))) and np.all(np.isfinite(device_to_f64(lse)))
-    _full(c, "large logits", exact_bars=False)
+    _full(c, f"large logits/{form}", exact_bars=False, n_rows=n)

@@ -88,10 +88,14 @@ def test_fp8_mfma_and_no_packed_fp32(isa_fp8):
     assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", isa_fp8)
 
 
-@pytest.mark.parametrize("instance", ["attn_fwd_fp8_kernelILb0E", "attn_fwd_fp8_kernelILb1E"])
+SKIP_INSTANCE = "attn_fwd_fp8_kernelILb1ELb0E"
+
+
+@pytest.mark.parametrize("instance", ["attn_fwd_fp8_kernelILb0ELb0E", "attn_fwd_fp8_kernelILb0ELb1E", SKIP_INSTANCE])
 def test_fp8_main_loop_has_no_spills_or_block_copies(isa_fp8, instance):
-    # both instances (dense, and with Skip-Softmax) store nothing to scratch in the loop and reload
-    # at most eight dwords per pass of the unrolled loop
+    # every instance (dense with the early or the late reference form, and with Skip-Softmax)
+    # stores nothing to scratch in the loop and reloads at most eight dwords per pass of the
+    # unrolled loop
     blocks = _loop_blocks(isa_fp8, instance)
     assert len(blocks) >= 8
     reloads = 0
@@ -100,9 +104,9 @@ def test_fp8_main_loop_has_no_spills_or_block_copies(isa_fp8, instance):
         assert "scratch_store" not in text
         reloads += text.count("scratch_load")
     assert reloads <= 8
-    if instance.endswith("ILb1E"):
+    if instance == SKIP_INSTANCE:
         return
-    # The dense instance, the hot path: register-to-register moves, per tile (one MFMA block of the
+    # The dense instances, the hot path: register-to-register moves, per tile (one MFMA block of the
     # loop per tile), stay at a handful -- the start value of the score chains -- where copying an
     # accumulator block from one set of registers to another on every tile would take 16 or more.
     mfma_blocks = [bl for bl in blocks if any("v_mfma" in ln for ln in bl)]
