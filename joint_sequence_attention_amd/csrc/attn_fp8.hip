@@ -321,9 +321,10 @@ __global__ __launch_bounds__(256) void v_quant_fp8_kernel(const u32x4* __restric
 // nothing; otherwise the wave takes the tile's exact maximum, moves the
 // reference where needed, rescales O and l and recomputes the tile.
 // Skip-Softmax instance: every tile's maximum is taken for the skip rule
-// anyway, so the reference is the exact running maximum of the kept tiles.  Either way O and l share one reference, so the
-// result is softmax over the kept keys with P rounded relative to a reference
-// within a factor 1.75 of the running maximum.
+// anyway, so the reference is the exact running maximum of the kept tiles.
+// Either way O and l share one reference, so the result is softmax over the
+// kept keys with P rounded relative to a reference within a factor 1.75 of
+// the running maximum.
 //
 // LDS: rings of eight key slots and eight value slots of 8 KiB.  Iteration t
 // reads K(t+1) and V(t-1) and issues direct buffer->LDS loads of K(t+5) and
@@ -680,7 +681,9 @@ __global__ __launch_bounds__(F8_NW * 64, 1) void attn_fwd_fp8_kernel(
   // into sc[1 - B] (consecutive pairs share the query operand); slots 4..7
   // issue O += V(t-1) P(t-1), one MFMA per 32-dim block of O^T (all four
   // share the probabilities).  Exponential unit j of tile t follows slot j,
-  // then tile t settles.  Two fragment registers alternate, each read one or
+  // then tile t settles; the early dense form moves the reference for tile t
+  // first (prepare) and takes the lane's maximum of S(t+1) in slots 5 and 6.
+  // Two fragment registers alternate, each read one or
   // two slots ahead of its MFMA (the first two at the start).  A scheduling
   // fence after every slot keeps this order.  The Skip-Softmax instance keeps
   // the MFMA order but groups the exponentials: units 0..3 after the score
