@@ -244,3 +244,59 @@ def compare_fp8(out_gpu, lse_gpu, out_sage, lse_sage, scales, out_exact, lse_exa
         assert stats["exact_lse_max"] <= FP8_EXACT_LSE_MAX, (label, stats)
         assert stats["exact_rel_max"] <= FP8_EXACT_REL, (label, stats, np.unravel_index(rel.argmax(), rel.shape))
     return stats
+
+
+BF16_NAN = 0x7FC0
+BF16_INF = 0x7F80
+
+
+def nonfinite_isolation(c, run, segments_poisoned=(1, 3, 6), same_row_heads=True, near=(1e-2, 1e-3)):
+    """Non-finite inputs stay where they are.
+
+    On a case built from ragged_segments(), poisons head 0 of one query row of segment 1 (NaN),
+    one key of segment 3 (+inf) and one value of segment 6 (NaN, value dim 100), and checks
+    against a clean run: every row of every other segment, and every other head, comes out bit
+    for bit the same; so does every other value dim of segment 6; the poisoned query row and
+    value dim do come out non-finite.  The other rows of the query's segment come out bit for bit
+    the same where the kernel decides everything per row (same_row_heads), else finite and within
+    near = (out, lse) max-abs of the clean run: a kernel that moves the softmax reference of a
+    whole wave at once may then round them against another valid reference.
+    run(c) -> (out, lse) on the case's current inputs.
+    """
+    sq, sk, sv = segments_poisoned
+    out0, lse0 = run(c)
+    o0, l0 = bf16_bits(out0), lse0.cpu().numpy()
+    rq, rk, rv = int(c.cu[sq]) + 5, int(c.cu[sk]) + 17, int(c.cu[sv]) + 40
+    assert rq < c.cu[sq + 1] and rk < c.cu[sk + 1] and rv < c.cu[sv + 1]
+    c.qb = c.qb.copy()
+    c.kb = c.kb.copy()
+    c.vb = c.vb.copy()
+    c.qb[rq, 0, 3] = BF16_NAN
+    c.kb[rk, 0, 10] = BF16_INF
+    c.vb[rv, 0, 100] = BF16_NAN
+    dev = c.q.device
+    c.q, c.k, c.v = bits_to_device(c.qb, dev), bits_to_device(c.kb, dev), bits_to_device(c.vb, dev)
+    out1, lse1 = run(c)
+    o1, l1 = bf16_bits(out1), lse1.cpu().numpy()
+    seg_of = np.searchsorted(c.cu, np.arange(c.N), side="right") - 1
+    clean = ~np.isin(seg_of, segments_poisoned)
+    assert np.array_equal(o1[clean], o0[clean]) and np.array_equal(l1[:, clean], l0[:, clean])
+    assert np.array_equal(o1[:, 1:], o0[:, 1:]) and np.array_equal(l1[1:], l0[1:])  # other heads
+    seg_v = seg_of == sv
+    keep = np.ones(o0.shape[2], dtype=bool)
+    keep[100] = False
+    assert np.array_equal(o1[seg_v][:, 0][:, keep], o0[seg_v][:, 0][:, keep])
+    f1 = widen(o1)
+    assert not np.all(np.isfinite(f1[rq, 0])) and not np.isfinite(l1[0, rq])
+    assert not np.all(np.isfinite(f1[seg_v, 0, 100]))
+    rows_q = (seg_of == sq) & (np.arange(c.N) != rq)
+    if same_row_heads:
+        # the other rows of the query's segment do not see its query at all
+        assert np.array_equal(o1[rows_q], o0[rows_q]) and np.array_equal(l1[:, rows_q], l0[:, rows_q])
+    else:
+        d_out = float(np.abs(widen(o1[rows_q]) - widen(o0[rows_q])).max())
+        d_lse = float(np.abs(l1[:, rows_q] - l0[:, rows_q]).max())
+        say(f"non-finite inputs: other rows of the query's segment moved by out {d_out:.3e}, lse {d_lse:.3e}")
+        assert d_out <= near[0] and d_lse <= near[1], (d_out, d_lse)
+    say(f"non-finite inputs: {int(clean.sum())} rows of untouched segments and heads 1.. bit for bit unchanged; "
+        f"poisoned row lse {l1[0, rq]}")

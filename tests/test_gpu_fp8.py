@@ -19,7 +19,8 @@ the bench times.
 import numpy as np
 import pytest
 
-from helpers import Case, bf16_bits, compare_fp8, device_to_f64, ragged_segments, say, widen
+from helpers import (Case, bf16_bits, compare_fp8, device_to_f64, nonfinite_isolation, ragged_segments, say,
+                     widen)
 from joint_sequence_attention_amd import h3attn as H
 from joint_sequence_attention_amd import workloads as wl
 
@@ -383,3 +384,15 @@ def test_fp8_very_large_logits(gpu, form):
     out, lse = c.run_fp8()
     assert np.all(np.isfinite(device_to_f64(out))) and np.all(np.isfinite(device_to_f64(lse)))
     _full(c, f"large logits/{form}", exact_bars=False, n_rows=n)
+
+
+@pytest.mark.parametrize("form", FORMS + ["skip"])
+def test_fp8_nonfinite_inputs_stay_in_their_segment(gpu, form):
+    # as for the exact path; the late form and Skip-Softmax decide some steps per wave, so there
+    # the other rows of the NaN query's wave may round differently and only other segments and
+    # heads are compared
+    c, _ = _form_case(ragged_segments(), 2, 178, "late" if form == "late" else "early")
+    thr = 0.05 if form == "skip" else 0.0
+    say(f"fp8 non-finite inputs ({form})")
+    nonfinite_isolation(c, lambda c: c.run_fp8(skip_threshold=thr), same_row_heads=(form == "early"),
+                        near=(0.05, 1e-2))

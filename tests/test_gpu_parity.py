@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import Case, bf16_bits, compare, device_to_f64, ragged_segments, say, widen
+from helpers import Case, bf16_bits, compare, device_to_f64, nonfinite_isolation, ragged_segments, say, widen
 from joint_sequence_attention_amd import h3attn as H
 from joint_sequence_attention_amd import workloads as wl
 
@@ -375,3 +375,11 @@ def test_short_max_seqlen_truncates_longer_segments(gpu, fp8):
     if not fp8:
         o_ref, l_ref = oracle.attention(widen(c.qb[keep]), widen(c.kb[keep]), widen(c.vb[keep]), cu_t, c.pos[keep])
         compare(device_to_f64(o_t), device_to_f64(l_t), o_ref, l_ref, label="short max_seqlen")
+
+
+def test_nonfinite_inputs_stay_in_their_segment(gpu):
+    # a NaN query, an infinite key and a NaN value, each in its own segment, change nothing
+    # outside their segment; the NaN row makes its wave take the rare path that moves every row's
+    # reference to its exact running maximum, so the other rows of that wave round against it
+    c = Case(ragged_segments(), 2, 177)
+    nonfinite_isolation(c, lambda c: c.run(), same_row_heads=False)
