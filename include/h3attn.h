@@ -148,6 +148,12 @@ h3attn_status h3attn_rope_apply(const void* x, void* y, const float* pos_thw, in
  * fp16 with power-of-two block scales (one per query row, one per 64-key
  * tile), which keeps bf16's range; probabilities and values enter the second
  * contraction as bf16; all accumulation is fp32.
+ *
+ * Inputs are not scanned.  A NaN or infinity in q makes that row's out and
+ * lse undefined, in k or v those of the rows of its segment (of one head);
+ * other segments and heads come out exactly as without it, and so, up to the
+ * rounding of their shared softmax reference, do the other rows of the
+ * segment.  The same holds for the FP8 mode below.
  * ------------------------------------------------------------------- */
 size_t h3attn_varlen_fwd_workspace_size(int64_t n_tokens, int32_t n_heads, int32_t head_dim, int32_t n_seqs);
 
