@@ -72,9 +72,9 @@ constexpr int F8_NS = 8;                 // slots per ring
 constexpr int F8_VBASE = F8_NS * F8_TILE_BYTES;
 constexpr size_t F8_SMEM = 2 * F8_NS * F8_TILE_BYTES;  // 128 KiB
 constexpr float P_SHIFT = 8.0f;          // probabilities are stored as p * 2^8, p relative to the row maximum
-constexpr float E4M3_TOP = 448.0f;       // largest finite e4m3 value
 // A stored probability p' = 2^(z - mm) with z the base-2 logit and mm the
-// running reference minus 8; it must not exceed 448, i.e. z - mm <= log2 448.
+// running reference minus 8; it must not exceed 448 (the largest finite e4m3
+// value), i.e. z - mm <= log2 448.
 // The reference is moved when that could fail; 8.75 < log2 448 = 8.807 leaves
 // room for the rounding of the exponent's argument.
 constexpr float P_ROOM_LOG2 = 8.75f;
